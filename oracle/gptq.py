@@ -1,0 +1,102 @@
+"""GPTQ, two independent routes.  TEST INFRASTRUCTURE ONLY.
+
+Both routes quantize the columns of W [d_o x d_i] one at a time in a common order
+shared by every row, each row against its own static grid (the grid is an input of
+the algorithm: GPTQ tutorial page, section 3, Algorithm 1 inputs; the ADMM-Q page's
+grid-refresh item notes that GPTQ keeps the grid fixed).
+
+* gptq_plain -- the definition.  GPTQ tutorial page, section 2, "a Lagrange multiplier
+  gives the compensation direction": fixing coordinate q to its grid value changes it
+  by d; the free coordinates move by -d H_F^{-1} e_q / (H_F^{-1})_qq, where H_F^{-1} is
+  the inverse curvature of the still-free coordinates, after which q leaves the free
+  set (the rank-one downdate of the inverse).
+* gptq -- the blocked route of the same page, section 3 (Algorithm 1): R is the upper
+  Cholesky factor of the damped inverse curvature (R^T R = H^{-1}); within a block of
+  B columns each column is rounded, its scaled error E = (w - q) / R_jj is stored and
+  the rest of the block is corrected by E R[j, j:b]; after the block the remaining
+  columns get one product update W[:, b:] -= E R[a:b, b:].
+
+H passed here already holds the damping (the Hessian builder adds lambda I once).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .grid import round_codes
+
+
+def inverse_factor(H: np.ndarray) -> np.ndarray:
+    """Upper-triangular R with R^T R = H^{-1}: invert, then take the Cholesky factor
+    (GPTQ tutorial page, section 3: R = upper Cholesky((H + lambda I)^{-1}))."""
+    Hinv = np.linalg.inv(np.asarray(H, np.float64))
+    Hinv = 0.5 * (Hinv + Hinv.T)
+    return np.linalg.cholesky(Hinv).T
+
+
+def _column_grid(scale, zero, group, col):
+    g = col // group
+    return np.asarray(scale[:, g], np.float64), np.asarray(zero[:, g], np.float64)
+
+
+def gptq_plain(H, W_hat, scale, zero, bits, group, order=None, clip=True):
+    """Lagrange / rank-one-downdate route.  Returns integer codes [d_o x d_i] in the
+    original column positions."""
+    W = np.array(W_hat, np.float64)
+    d_o, d_i = W.shape
+    order = np.arange(d_i) if order is None else np.asarray(order)
+    Hinv = np.linalg.inv(np.asarray(H, np.float64))
+    free = list(order)
+    codes = np.zeros((d_o, d_i), np.int64)
+    for col in order:
+        s, z = _column_grid(scale, zero, group, col)
+        c, _, _ = round_codes(W[:, col] / s, z, bits, clip)
+        codes[:, col] = c
+        d = W[:, col] - s * (c - z)               # w_q - quant(w_q)
+        idx = np.array(free)
+        k = free.index(col)
+        hq = Hinv[np.ix_(idx, [col])][:, 0]      # (H_F^{-1})_{F,q}
+        W[:, idx] -= np.outer(d / Hinv[col, col], hq)
+        # downdate: H_F^{-1} <- H_F^{-1} - H_F^{-1} e_q e_q^T H_F^{-1} / (H_F^{-1})_qq
+        Hinv[np.ix_(idx, idx)] -= np.outer(hq, hq) / Hinv[col, col]
+        free.pop(k)
+    return codes
+
+
+def gptq(H, W_hat, scale, zero, bits, group, B, order=None, clip=True,
+         hint=None, tol=1e-4, R=None, return_E=False):
+    """Blocked route (Algorithm 1 of the GPTQ tutorial page).
+
+    order: processing order of the original columns (None = natural).  The factor R
+    belongs to the reordered curvature H[order][:, order]; pass it to skip the
+    factorisation.  hint: codes [d_o x d_i] (original positions) used only at
+    near-boundary elements (oracle.grid.round_codes).  Returns (codes, adoptions)
+    and, with return_E, the scaled errors E [d_o x d_i] in processing order."""
+    W_hat = np.asarray(W_hat, np.float64)
+    d_o, d_i = W_hat.shape
+    order = np.arange(d_i) if order is None else np.asarray(order)
+    if R is None:
+        Hp = np.asarray(H, np.float64)[np.ix_(order, order)]
+        R = inverse_factor(Hp)
+    W = W_hat[:, order].copy()
+    codes = np.zeros((d_o, d_i), np.int64)
+    Eall = np.zeros((d_o, d_i)) if return_E else None
+    adopted = 0
+    for a in range(0, d_i, B):
+        b = min(a + B, d_i)
+        E = np.zeros((d_o, b - a))
+        for j in range(a, b):
+            col = order[j]
+            s, z = _column_grid(scale, zero, group, col)
+            h = None if hint is None else hint[:, col]
+            c, n, _ = round_codes(W[:, j] / s, z, bits, clip, h, tol)
+            adopted += n
+            codes[:, col] = c
+            q = s * (c - z)
+            E[:, j - a] = (W[:, j] - q) / R[j, j]
+            W[:, j:b] -= np.outer(E[:, j - a], R[j, j:b])
+        W[:, b:] -= E @ R[a:b, b:]
+        if return_E:
+            Eall[:, a:b] = E
+    if return_E:
+        return codes, adopted, Eall
+    return codes, adopted
