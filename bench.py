@@ -1,0 +1,233 @@
+"""Benchmark of the layer quantizer's hot path on one MI355X.
+
+One step = one pass of the whole path over one layer: Hessian build from the
+calibration tokens, GPTQ (grid, inverse factor, column loop), ADMM-Q (one-time
+eigendecomposition, then the iteration loop) and packing of both results.
+Inputs (calibration activations and weights) are synthetic, seeded, and resident in
+HBM before the timed region starts.
+
+The headline value is ADMM-Q iterations per second of the loop (set-up and the
+eigendecomposition excluded, they are reported separately), next to the GPTQ layer
+time and the Hessian TFLOP/s.  Per-kernel durations come from the library's HIP
+events (qz_timing_*), recorded on the stream the kernels run on.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import qz_synth  # noqa: E402
+
+METRIC = "ADMM-Q iters/s + GPTQ layer time, 4096×12288 W3g128; H-build TFLOP/s"
+HEADLINE = "up_4096x12288_w3g128"
+
+PEAK_BF16 = 2.5e15        # dense MFMA, FLOP/s
+PEAK_FP32_MFMA = 157.3e12
+PEAK_HBM = 8.0e12         # B/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(qz_synth.WORKLOADS))
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--cpu-iters", type=int, default=10)
+    return ap.parse_args()
+
+
+def cpu_baseline(cfg, X, W_bits, rows, iters):
+    """The fp64 oracle on the host: ADMM-Q iterations on a sample of rows (rows are
+    independent), scaled to the whole layer; the eigendecomposition is excluded as
+    it is on the GPU.  H comes from the oracle on the same tokens."""
+    import numpy as np
+    from oracle import admm, hessian
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=os.cpu_count())
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count()
+    n_sample = min(X.shape[0], 16384)
+    Xs = X[:n_sample]
+    t0 = time.perf_counter()
+    H, _ = hessian.hessian(Xs, cfg["damp"])
+    t_h = time.perf_counter() - t0
+    spec = admm.spectral(H)
+    Wf = qz_synth.bf16_bits_to_f32(W_bits[:rows])
+    t0 = time.perf_counter()
+    admm.admm(H, Wf, cfg["bits"], cfg["group"], iters, cfg["rho0"], cfg["gamma"], cfg["refresh"],
+              spec=spec)
+    t_loop = time.perf_counter() - t0
+    per_iter_layer = t_loop / iters * (cfg["d_o"] / rows)
+    return {"value": 1.0 / per_iter_layer, "unit": "iters/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{rows} of {cfg['d_o']} rows x {iters} ADMM iterations (fp64 NumPy, H from "
+                      f"{n_sample} tokens, eigendecomposition excluded), scaled to the full layer; "
+                      f"loop {t_loop:.2f} s, H build {t_h:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the quantizer's rows shard "
+              f"across GPUs without per-iteration exchange, but no multi-GPU path is built.",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import post_weight_quantization_05_amd as q
+
+    cfg = dict(qz_synth.WORKLOADS[args.workload])
+    d_i, d_o, n = cfg["d_i"], cfg["d_o"], cfg["n"]
+    bits, group, B, iters = cfg["bits"], cfg["group"], cfg["B"], cfg["iters"]
+    seed = cfg.get("seed", 1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---- inputs resident in HBM
+    X = qz_synth.calib_bf16_torch(seed, n, d_i, cfg["p_out"], cfg["f_out"], device=dev)
+    W = qz_synth.weights_bf16_torch(seed, d_o, d_i, device=dev)
+    H = torch.empty((d_i, d_i), dtype=torch.float32, device=dev)
+    ws_h = torch.empty(max(q.qz_hessian_workspace(n, d_i), 1), dtype=torch.uint8, device=dev)
+    ws_g = torch.empty(q.qz_gptq_workspace(d_o, d_i, B), dtype=torch.uint8, device=dev)
+    ws_a = torch.empty(q.qz_admmq_workspace(d_o, d_i, group, iters), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def step(record):
+        e = [ev() for _ in range(7)]
+        e[0].record(stream)
+        hb = q.qz_build_hessian(X, damp=cfg["damp"], H=H, ws=ws_h)
+        e[1].record(stream)
+        gc, gs, gz = q.qz_gptq(hb["H"], W, bits, group, B, ws=ws_g)
+        e[2].record(stream)
+        gp = q.qz_pack(gc, bits)
+        e[3].record(stream)
+        V, lam, sig = q.qz_admmq_prepare(hb["H"])
+        e[4].record(stream)
+        out = q.qz_admmq(V, lam, sig, W, bits, group, iters, cfg["rho0"], cfg["gamma"],
+                         cfg["refresh"], ws=ws_a, want_U=False)
+        e[5].record(stream)
+        ap = q.qz_pack(out["codes"], bits)
+        e[6].record(stream)
+        if record is not None:
+            record.append((e, out["residuals"]))
+        return gp, ap
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+
+    q.qz_timing_read(reset=True)
+    q.qz_timing_enable(True)
+    recs = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(recs)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    q.qz_timing_enable(False)
+    kt = q.qz_timing_read(reset=True)
+
+    # ---- per-phase times (ms) from the events
+    ph = {k: [] for k in ("hbuild", "gptq", "pack_gptq", "admm_prepare", "admm", "pack_admm")}
+    for e, _ in recs:
+        vals = [e[i].elapsed_time(e[i + 1]) for i in range(6)]
+        for k, v in zip(ph, vals):
+            ph[k].append(v)
+    med = {k: float(np.median(v)) for k, v in ph.items()}
+    admm_loop_ms = 0.0
+    # the ADMM call's loop = its kernels minus the one-time set-up product
+    kn = {k: v for k, v in kt.items()}
+    loop_kinds = ("gemm_admm_wupdate1", "gemm_admm_wupdate2", "admm_project")
+    admm_loop_ms = sum(kn[k][1] for k in loop_kinds if k in kn) / args.steps
+    admm_call_ms = med["admm"]
+    iters_per_s = iters / (admm_call_ms / 1e3)
+    iters_per_s_loop = iters / (admm_loop_ms / 1e3) if admm_loop_ms > 0 else None
+
+    # ---- rooflines (algorithmic work per launch / average launch duration)
+    def avg_ms(kind):
+        c, t = kn.get(kind, (0, 0.0))
+        return t / c if c else None
+
+    gemm_flops = 2.0 * d_o * d_i * d_i                      # one W-update product
+    proj_bytes = 18.0 * d_o * d_i                           # read W~,U,C_old; write U,M,C
+    hb_flops = 1.0 * n * d_i * (d_i + 1)                    # upper triangle of X^T X
+    rl = []
+    for kind, work, peak, bound, unit in (
+            ("gemm_admm_wupdate1", gemm_flops, PEAK_FP32_MFMA, "mfma", "TFLOP/s"),
+            ("gemm_admm_wupdate2", gemm_flops, PEAK_FP32_MFMA, "mfma", "TFLOP/s"),
+            ("admm_project", proj_bytes, PEAK_HBM, "hbm", "GB/s"),
+            ("hessian_gram_bf16", hb_flops, PEAK_BF16, "mfma", "TFLOP/s")):
+        a = avg_ms(kind)
+        if a is None:
+            continue
+        rate = work / (a / 1e3)
+        scale = 1e12 if unit == "TFLOP/s" else 1e9
+        rl.append({"kernel": kind, "bound": bound, "achieved": round(rate / scale, 3),
+                   "peak": round(peak / scale, 3), "unit": unit, "frac": round(rate / peak, 4),
+                   "avg_ms": round(a, 4), "launches": kn[kind][0], "traffic": None})
+    dominant = max((r for r in rl if r["kernel"].startswith("gemm_admm")),
+                   key=lambda r: r["avg_ms"] * r["launches"], default=None)
+
+    res_last = recs[-1][1][-1].tolist() if recs else None
+    gptq_ms = med["gptq"]
+    line = {
+        "metric": METRIC,
+        "value": round(iters_per_s, 3),
+        "unit": "iters/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "d_i": d_i, "d_o": d_o, "bits": bits, "group": group,
+                   "n_tokens": n, "gptq_block": B, "admm_iters": iters, "rho0": cfg["rho0"],
+                   "gamma": cfg["gamma"], "refresh_every": cfg["refresh"],
+                   "global_batch": n, "parallelism": "single-gpu"},
+        "components": {
+            "admm_iters_per_s": round(iters_per_s, 3),
+            "admm_iters_per_s_kernels_only": None if iters_per_s_loop is None else round(iters_per_s_loop, 3),
+            "admm_call_ms": round(admm_call_ms, 3),
+            "admm_prepare_ms": round(med["admm_prepare"], 3),
+            "admm_weights_per_s": round(d_o * d_i / ((admm_call_ms + med["admm_prepare"]) / 1e3), 1),
+            "gptq_layer_ms": round(gptq_ms, 3),
+            "gptq_weights_per_s": round(d_o * d_i / (gptq_ms / 1e3), 1),
+            "gptq_rfactor_ms": round(avg_ms("rfactor_fp64") or 0.0, 3),
+            "hbuild_ms": round(med["hbuild"], 3),
+            "hbuild_tflops": round(hb_flops / (med["hbuild"] / 1e3) / 1e12, 3),
+            "pack_ms": round(med["pack_gptq"] + med["pack_admm"], 4),
+            "admm_final_residuals": res_last,
+            "kernel_ms": {k: [v[0], round(v[1] / max(v[0], 1), 4)] for k, v in kn.items()},
+        },
+        "rooflines": rl,
+        "roofline": None if dominant is None else {k: dominant[k] for k in
+                                                   ("bound", "achieved", "peak", "unit", "frac",
+                                                    "traffic")} | {"kernel": dominant["kernel"]},
+    }
+    if not args.no_cpu:
+        Xh = X[:16384].view(torch.int16).cpu().numpy().view(np.uint16)
+        Wh = W[:args.cpu_rows].view(torch.int16).cpu().numpy().view(np.uint16)
+        line["cpu_baseline"] = cpu_baseline(cfg, Xh, Wh, args.cpu_rows, args.cpu_iters)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

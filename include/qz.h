@@ -1,0 +1,235 @@
+/*
+ * qz.h -- C ABI of libqz, a Hessian-weighted layer-wise weight quantizer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library solves, for one linear layer with pretrained weights W_hat
+ * [d_o x d_i] (row-major, one row per output channel) and calibration
+ * activations X [n x d_i],
+ *
+ *     min_W  1/2 Tr((W - W_hat) H (W - W_hat)^T)   s.t. W on a b-bit grid,
+ *     H = X^T X + lambda I,
+ *
+ * ("ADMM-Q: An Improved Hessian-based Weight Quantizer for Post-Training
+ * Quantization of Large Language Models", technical summary, 1. problem
+ * formulation; the pages store W as d_i x d_o, this ABI stores the transpose,
+ * which leaves the objective unchanged) with two solvers: GPTQ ("061 · GPTQ"
+ * tutorial, section 3, Algorithm 1) and ADMM-Q (ADMM-Q summary, 2. key
+ * algorithmic components).
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - All array arguments are DEVICE pointers unless the comment says "host".
+ *   The caller owns every buffer; the library never frees caller memory.
+ *   Work buffers come from the caller through `ws`/`ws_bytes`, sized by the
+ *   matching *_workspace() query; a smaller buffer gives QZ_EWORKSPACE.
+ *   (qz_admmq_prepare is the exception: the eigen-solver library it calls
+ *   manages its own device memory.)
+ * - Matrices are dense row-major with the leading dimension equal to the
+ *   column count, unless an ld argument is given.
+ * - Arguments are checked before anything is enqueued; on a non-OK return the
+ *   outputs are unspecified.
+ * - Work is enqueued on `stream` (0 = the default stream).  Calls return after
+ *   enqueueing unless marked SYNC; a SYNC call waits for its own work on
+ *   `stream` and reports device-side failures (non-positive-definite H,
+ *   non-finite data) through its status.
+ * - Results are deterministic: no floating-point atomics are used, so two
+ *   calls on the same inputs give the same bytes.
+ * - qz_last_error() returns a thread-local message for the last non-OK status
+ *   returned on the calling thread.
+ */
+#ifndef QZ_H
+#define QZ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QZ_ABI_VERSION 1
+
+typedef enum {
+  QZ_OK = 0,
+  QZ_EINVAL = -1,       /* bad argument (null pointer, size, bits, group, ...) */
+  QZ_ENOTPD = -2,       /* H is not positive definite (add damping)            */
+  QZ_ENONFINITE = -3,   /* NaN or Inf in H, W_hat or the ADMM iterates          */
+  QZ_EHIP = -4,         /* a HIP runtime call failed                             */
+  QZ_ESOLVER = -5,      /* the eigen-solver library failed                      */
+  QZ_EWORKSPACE = -6    /* workspace too small                                   */
+} qz_status;
+
+typedef enum { QZ_BF16 = 0, QZ_F32 = 1 } qz_dtype;
+
+/* ------------------------------------------------------------------ grid --
+ * Per (row, group of `group_size` consecutive input columns) asymmetric grid:
+ * value(c) = s * (c - z), c in {0 .. 2^bits - 1}, s fp32, z u8.
+ * Fit rule (the pages give none; this is the library's reading): over the
+ * group, lo = min(min v, 0), hi = max(max v, 0) (an all-zero group uses
+ * [-1, 1]); s = fl32(fl32(hi - lo) / (2^b - 1)); z = clamp(rint(fl32(-lo/s)),
+ * 0, 2^b - 1).  Codes: c = clamp(rint(fl32(x / s)) + z, 0, 2^b - 1), rint =
+ * round half to even, IEEE fp32 division.  Scales and zeros are [d_o x d_i/g]
+ * row-major.                                                                  */
+#define QZ_GRID_CALLER 0x1u   /* scales/zeros are inputs, not fit from W_hat */
+
+typedef struct {
+  uint32_t struct_size;   /* sizeof(qz_grid) */
+  int32_t bits;           /* 2 .. 8 */
+  int32_t group_size;     /* >= 1, divides d_i; group_size == d_i is per output channel */
+  uint32_t flags;         /* QZ_GRID_CALLER */
+} qz_grid;
+
+/* ---------------------------------------------------------------- Hessian --
+ * qz_build_hessian: H = X^T X + lambda I with lambda = damp * mean(diag(X^T X))
+ * (ADMM-Q summary, 1. problem formulation; damping: GPTQ tutorial, section 2,
+ * "why damping is needed when calibration channels are collinear"), plus
+ * diag(H) and Sigma = diag(H)^(-1/2) (ADMM-Q summary, 2., diagonal scaling).
+ *
+ *   X       [n x d_i], dtype xt (QZ_BF16: bf16 bit patterns; QZ_F32), n >= 1.
+ *   flags   QZ_H_ACCUMULATE: add this call's X^T X to the unfinalised sum
+ *             already in H (from a call made with QZ_H_NO_FINALIZE), so long
+ *             calibration sets can be fed in token chunks;
+ *           QZ_H_NO_FINALIZE: leave the raw sum X^T X in the UPPER triangle of
+ *             H (lower triangle unspecified), no damping, diag/sigma/lambda
+ *             untouched.
+ *           Without QZ_H_NO_FINALIZE the call finishes H: mirrors it to a full
+ *           symmetric matrix, adds lambda I and writes diag, sigma, lambda.
+ *   H       [d_i x d_i] fp32 output (in/out with QZ_H_ACCUMULATE).
+ *   diag, sigma  [d_i] fp32 outputs (nullable); lambda_out: 1 fp32 (nullable).
+ * Products of bf16 values are exact in fp32; sums are fp32 (matrix cores).
+ * Asynchronous.  Non-finite X gives non-finite H, which qz_gptq and
+ * qz_admmq_prepare report as QZ_ENONFINITE.                                 */
+#define QZ_H_ACCUMULATE 0x1u
+#define QZ_H_NO_FINALIZE 0x2u
+
+size_t qz_hessian_workspace(int64_t n, int64_t d_i, int32_t xt);
+int qz_build_hessian(const void* X, int32_t xt, int64_t n, int64_t d_i, float damp,
+                     uint32_t flags, float* H, float* diag, float* sigma, float* lambda_out,
+                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* -------------------------------------------------------------------- RTN --
+ * qz_rtn: round-to-nearest of every weight on its own (ADMM-Q summary, problem
+ * statement), on the grid fit from W (or the caller's grid with
+ * QZ_GRID_CALLER).  Bit-exact with the fp32 definition above.
+ *   W [d_o x d_i] (dtype wt); codes [d_o x d_i] u8 out; scales/zeros
+ *   [d_o x d_i/g] out (in with QZ_GRID_CALLER).  SYNC (reports non-finite W). */
+int qz_rtn(const void* W, int32_t wt, int64_t d_o, int64_t d_i, const qz_grid* grid,
+           uint8_t* codes, float* scales, uint8_t* zeros, hipStream_t stream);
+
+/* ------------------------------------------------------------------- GPTQ --
+ * qz_gptq: GPTQ tutorial, section 3 (Algorithm 1).  R is the upper Cholesky
+ * factor of H^{-1} (H already damped by qz_build_hessian; no damping is added
+ * here).  Columns are processed in blocks of B in a common order for all rows
+ * (`perm`, or natural order); in each block every column is rounded on its
+ * row's static grid, E = (w - q) / R_jj is kept and the block's remaining
+ * columns get E R[j, j:b]; after the block the trailing columns get one
+ * matrix-core product update W[:, b:] -= E R[a:b, b:].
+ *   H      [d_i x d_i] fp32 symmetric positive definite.
+ *   W_hat  [d_o x d_i] (dtype wt).
+ *   B      block size, 1 .. 128.
+ *   perm   [d_i] int32 processing order (a permutation of 0..d_i-1) or NULL.
+ *          Groups are always contiguous ranges of the ORIGINAL columns, and
+ *          codes are written in original column positions.
+ *   codes  [d_o x d_i] u8 out; scales/zeros [d_o x d_i/g] out (in with
+ *          QZ_GRID_CALLER).
+ * R is computed in fp64 (blocked Cholesky of the reversed H, triangular
+ * inverse) and used in fp32.  SYNC: returns QZ_ENOTPD when a pivot of the
+ * factorisation is <= 1e-12 of its diagonal entry (or not finite), and
+ * QZ_ENONFINITE for non-finite W_hat.                                       */
+size_t qz_gptq_workspace(int64_t d_o, int64_t d_i, int32_t B);
+int qz_gptq(const float* H, const void* W_hat, int32_t wt, int64_t d_o, int64_t d_i,
+            const qz_grid* grid, int32_t B, const int32_t* perm,
+            uint8_t* codes, float* scales, uint8_t* zeros,
+            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ----------------------------------------------------------------- ADMM-Q --
+ * qz_admmq_prepare: Sigma = diag(H)^(-1/2), H~ = Sigma H Sigma and its
+ * eigendecomposition H~ = V diag(Lambda) V^T (ADMM-Q summary, 2.: the
+ * W-update is evaluated through an eigendecomposition of the Hessian).  The
+ * decomposition runs in fp64 in the rocSOLVER library (a library call standing
+ * in for host LAPACK); V and Lambda are returned in fp32.
+ *   H [d_i x d_i] fp32; V [d_i x d_i] fp32 out, V[j][k] = component j of
+ *   eigenvector k; Lambda [d_i] ascending; sigma [d_i].  SYNC.               */
+int qz_admmq_prepare(const float* H, int64_t d_i, float* V, float* Lambda, float* sigma,
+                     hipStream_t stream);
+
+/* qz_admmq: the ADMM-Q splitting loop in scaled coordinates W~ = W Sigma^{-1}:
+ *   for t = t0 .. t0+iters-1, rho_t = rho0 * gamma^t (ADMM-Q summary, 2.,
+ *   convergence under the penalty schedule):
+ *     M  = D~ - U
+ *     W~ = ((P + rho_t M V) diag(1/(Lambda + rho_t))) V^T, P = W~_hat V Lambda
+ *          (two fp32 matrix-core products)                         [W-update]
+ *     if refresh_every > 0 and t % refresh_every == 0: refit each group's grid
+ *          from min/max of the continuous iterate W~ Sigma, clamped into the
+ *          group's initial range [lo_0, hi_0]                  [grid refresh]
+ *     C  = codes of (W~ + U) Sigma, D~ = s (C - z) Sigma^{-1}      [D-update]
+ *     U  = (U + W~ - D~) * rho_t / rho_{t+1}                    [dual update]
+ *     residuals[t - t0] = (||W~ - D~||_F, rho_t ||D~ - D~_prev||_F)
+ *   Start (without QZ_ADMM_WARM_START): t0 = 0, the static grid fit from W_hat
+ *   (or the caller's with QZ_GRID_CALLER), C = RTN(W_hat), U = 0.
+ *   With QZ_ADMM_WARM_START the state (codes, scales, zeros, U) is read from
+ *   the output buffers and the loop resumes at p->t0.
+ *   Output: the last discrete iterate (codes) and its grid.
+ *   V, Lambda, sigma from qz_admmq_prepare.  U [d_o x d_i] fp32 in/out
+ *   (nullable unless WARM_START).  residuals [iters x 2] fp32 (nullable).
+ *   SYNC: QZ_ENONFINITE if W_hat is not finite or a residual became NaN.    */
+#define QZ_ADMM_WARM_START 0x1u
+#define QZ_ADMM_REFRESH_UNCLAMPED 0x2u  /* refit without the [lo_0, hi_0] clamp */
+#define QZ_ADMM_REFRESH_FROM_Z 0x4u     /* refit from (W~ + U) Sigma            */
+#define QZ_ADMM_DUAL_NO_RESCALE 0x8u    /* U = U + W~ - D~ (no rho_t/rho_{t+1}) */
+
+typedef struct {
+  uint32_t struct_size;   /* sizeof(qz_admm) */
+  int32_t iters;          /* >= 0 */
+  float rho0;             /* > 0 */
+  float gamma;            /* > 0 */
+  int32_t refresh_every;  /* 0 = never */
+  uint32_t flags;
+  int32_t t0;             /* first iteration index with QZ_ADMM_WARM_START */
+} qz_admm;
+
+size_t qz_admmq_workspace(int64_t d_o, int64_t d_i, int32_t group_size, int32_t iters);
+int qz_admmq(const float* V, const float* Lambda, const float* sigma,
+             const void* W_hat, int32_t wt, int64_t d_o, int64_t d_i,
+             const qz_grid* grid, const qz_admm* params,
+             uint8_t* codes, float* scales, uint8_t* zeros, float* U, float* residuals,
+             void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------- packing --
+ * Storage format (the ADMM-Q summary says the output keeps GPTQ's format; the
+ * bit layout is this library's reading): each row is a little-endian stream
+ * of 32-bit words, code i in bits [i*bits, (i+1)*bits), least significant bit
+ * first (codes may straddle words), zero-padded to ceil(cols*bits/32) words.
+ *   codes [rows x cols] u8 (every code < 2^bits); out [rows x words] u32.
+ * Asynchronous.                                                             */
+int64_t qz_packed_words(int64_t cols, int32_t bits);
+int qz_pack(const uint8_t* codes, int64_t rows, int64_t cols, int32_t bits, uint32_t* out,
+            hipStream_t stream);
+int qz_unpack(const uint32_t* in, int64_t rows, int64_t cols, int32_t bits, uint8_t* codes,
+              hipStream_t stream);
+
+/* ----------------------------------------------------------------- timing --
+ * Per-kernel timing for measurement tools: while enabled, the library records a
+ * HIP event pair around each of its kernel launches, on the stream the kernel
+ * runs on, and qz_timing_read sums the elapsed times per kernel kind.
+ *   qz_timing_enable(1) starts recording (calling process, any device); 0 stops.
+ *   qz_timing_read fills launches[k] and total_ms[k] for k < min(max_kinds,
+ *   QZ_TIMING_KINDS) (host arrays, may be NULL), waits for the recorded events
+ *   (SYNC), then, if reset != 0, drops the records.  Returns the number of kinds.
+ *   qz_timing_kind_name(k) names kind k ("" when out of range).              */
+#define QZ_TIMING_KINDS 16
+int qz_timing_enable(int on);
+int qz_timing_read(int64_t* launches, double* total_ms, int max_kinds, int reset);
+const char* qz_timing_kind_name(int kind);
+
+/* ---------------------------------------------------------------- misc ---- */
+const char* qz_last_error(void);
+int qz_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QZ_H */

@@ -1,0 +1,237 @@
+"""Python binding of libqz, the gfx950 HIP library behind include/qz.h.
+
+Argument marshalling only: tensors are allocated with PyTorch on the current CUDA
+(HIP) device, their pointers and the current stream are passed through ctypes, and
+every step of every solver runs in the library's kernels.  The functions carry the
+C names; see include/qz.h for the operation each one performs and its citation.
+
+Importing this package does not load the library; the first call does, and fails
+loudly if libqz.so has not been built (there is no CPU fallback).
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+from . import _lib
+from ._lib import (QZ_ADMM_DUAL_NO_RESCALE, QZ_ADMM_REFRESH_FROM_Z, QZ_ADMM_REFRESH_UNCLAMPED,  # noqa: F401
+                   QZ_ADMM_WARM_START, QZ_BF16, QZ_F32, QZ_GRID_CALLER, QZ_H_ACCUMULATE,
+                   QZ_H_NO_FINALIZE, QzAdmm, QzGrid)
+
+
+class QzError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        super().__init__(f"{_lib.STATUS_NAMES.get(status, status)}: {message}")
+
+
+def lib():
+    return _lib.load()
+
+
+def _check(status: int):
+    if status != 0:
+        raise QzError(status, lib().qz_last_error().decode(errors="replace"))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream():
+    torch = _torch()
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return _lib.QZ_BF16
+    if t.dtype == torch.float32:
+        return _lib.QZ_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _grid(bits, group, caller=False):
+    return QzGrid(C.sizeof(QzGrid), int(bits), int(group), _lib.QZ_GRID_CALLER if caller else 0)
+
+
+def _workspace(nbytes, device):
+    torch = _torch()
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def qz_abi_version() -> int:
+    return lib().qz_abi_version()
+
+
+def qz_hessian_workspace(n, d_i, xt=_lib.QZ_BF16) -> int:
+    return lib().qz_hessian_workspace(n, d_i, xt)
+
+
+def qz_build_hessian(X, damp=0.01, flags=0, H=None, ws=None):
+    """H = X^T X + lambda I (X [n x d_i] bf16 or fp32 on the GPU).  Returns
+    dict(H, diag, sigma, lam) (tensors; lam is a 1-element tensor)."""
+    torch = _torch()
+    _dev(X, "X")
+    n, d = X.shape
+    xt = _dtype_code(X)
+    dev = X.device
+    if H is None:
+        H = torch.empty((d, d), dtype=torch.float32, device=dev)
+    diag = torch.empty(d, dtype=torch.float32, device=dev)
+    sigma = torch.empty(d, dtype=torch.float32, device=dev)
+    lam = torch.empty(1, dtype=torch.float32, device=dev)
+    need = lib().qz_hessian_workspace(n, d, xt)
+    if ws is None:
+        ws = _workspace(need, dev)
+    _check(lib().qz_build_hessian(_ptr(X), xt, n, d, float(damp), int(flags), _ptr(H), _ptr(diag),
+                                  _ptr(sigma), _ptr(lam), _ptr(ws), ws.numel(), _stream()))
+    return dict(H=H, diag=diag, sigma=sigma, lam=lam)
+
+
+def qz_rtn(W, bits, group, scales=None, zeros=None):
+    """Round-to-nearest codes on the grid fit from W (or the given grid)."""
+    torch = _torch()
+    _dev(W, "W")
+    d_o, d_i = W.shape
+    caller = scales is not None
+    G = d_i // group if group > 0 and d_i % group == 0 else 0
+    if not caller:
+        scales = torch.empty((d_o, G), dtype=torch.float32, device=W.device)
+        zeros = torch.empty((d_o, G), dtype=torch.uint8, device=W.device)
+    codes = torch.empty((d_o, d_i), dtype=torch.uint8, device=W.device)
+    g = _grid(bits, group, caller)
+    _check(lib().qz_rtn(_ptr(W), _dtype_code(W), d_o, d_i, C.byref(g), _ptr(codes), _ptr(scales),
+                        _ptr(zeros), _stream()))
+    return codes, scales, zeros
+
+
+def qz_gptq_workspace(d_o, d_i, B) -> int:
+    return lib().qz_gptq_workspace(d_o, d_i, B)
+
+
+def qz_gptq(H, W_hat, bits, group, B=128, perm=None, scales=None, zeros=None, ws=None):
+    """GPTQ codes and grid for W_hat [d_o x d_i] given H [d_i x d_i]."""
+    torch = _torch()
+    _dev(H, "H")
+    _dev(W_hat, "W_hat")
+    d_o, d_i = W_hat.shape
+    caller = scales is not None
+    G = d_i // group if group > 0 and d_i % group == 0 else 0
+    if not caller:
+        scales = torch.empty((d_o, G), dtype=torch.float32, device=W_hat.device)
+        zeros = torch.empty((d_o, G), dtype=torch.uint8, device=W_hat.device)
+    codes = torch.empty((d_o, d_i), dtype=torch.uint8, device=W_hat.device)
+    if perm is not None:
+        perm = _dev(perm.to(torch.int32), "perm")
+    if ws is None:
+        ws = _workspace(lib().qz_gptq_workspace(d_o, d_i, B), W_hat.device)
+    g = _grid(bits, group, caller)
+    _check(lib().qz_gptq(_ptr(H), _ptr(W_hat), _dtype_code(W_hat), d_o, d_i, C.byref(g), int(B),
+                         _ptr(perm), _ptr(codes), _ptr(scales), _ptr(zeros), _ptr(ws), ws.numel(),
+                         _stream()))
+    return codes, scales, zeros
+
+
+def qz_admmq_prepare(H):
+    """(V, Lambda, sigma) with Sigma H Sigma = V diag(Lambda) V^T."""
+    torch = _torch()
+    _dev(H, "H")
+    d = H.shape[0]
+    V = torch.empty((d, d), dtype=torch.float32, device=H.device)
+    lam = torch.empty(d, dtype=torch.float32, device=H.device)
+    sigma = torch.empty(d, dtype=torch.float32, device=H.device)
+    _check(lib().qz_admmq_prepare(_ptr(H), d, _ptr(V), _ptr(lam), _ptr(sigma), _stream()))
+    return V, lam, sigma
+
+
+def qz_admmq_workspace(d_o, d_i, group, iters) -> int:
+    return lib().qz_admmq_workspace(d_o, d_i, group, iters)
+
+
+def qz_admmq(V, Lambda, sigma, W_hat, bits, group, iters, rho0, gamma, refresh_every=1, flags=0,
+             t0=0, state=None, scales=None, zeros=None, ws=None, want_U=True):
+    """ADMM-Q.  state: dict(codes, scales, zeros, U) to resume (sets QZ_ADMM_WARM_START;
+    the tensors are updated in place).  Returns dict(codes, scales, zeros, U, residuals)."""
+    torch = _torch()
+    for t, nm in ((V, "V"), (Lambda, "Lambda"), (sigma, "sigma"), (W_hat, "W_hat")):
+        _dev(t, nm)
+    d_o, d_i = W_hat.shape
+    dev = W_hat.device
+    G = d_i // group if group > 0 and d_i % group == 0 else 0
+    caller = scales is not None
+    if state is not None:
+        flags |= _lib.QZ_ADMM_WARM_START
+        codes, scales, zeros, U = state["codes"], state["scales"], state["zeros"], state["U"]
+    else:
+        codes = torch.empty((d_o, d_i), dtype=torch.uint8, device=dev)
+        if not caller:
+            scales = torch.empty((d_o, G), dtype=torch.float32, device=dev)
+            zeros = torch.empty((d_o, G), dtype=torch.uint8, device=dev)
+        U = torch.empty((d_o, d_i), dtype=torch.float32, device=dev) if want_U else None
+    res = torch.empty((max(iters, 1), 2), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = _workspace(lib().qz_admmq_workspace(d_o, d_i, group, iters), dev)
+    g = _grid(bits, group, caller)
+    p = QzAdmm(C.sizeof(QzAdmm), int(iters), float(rho0), float(gamma), int(refresh_every), int(flags),
+               int(t0))
+    _check(lib().qz_admmq(_ptr(V), _ptr(Lambda), _ptr(sigma), _ptr(W_hat), _dtype_code(W_hat), d_o,
+                          d_i, C.byref(g), C.byref(p), _ptr(codes), _ptr(scales), _ptr(zeros),
+                          _ptr(U), _ptr(res), _ptr(ws), ws.numel(), _stream()))
+    return dict(codes=codes, scales=scales, zeros=zeros, U=U, residuals=res[:iters])
+
+
+def qz_packed_words(cols, bits) -> int:
+    return lib().qz_packed_words(cols, bits)
+
+
+def qz_pack(codes, bits):
+    torch = _torch()
+    _dev(codes, "codes")
+    rows, cols = codes.shape
+    out = torch.empty((rows, max(lib().qz_packed_words(cols, bits), 0)), dtype=torch.int32,
+                      device=codes.device)
+    _check(lib().qz_pack(_ptr(codes), rows, cols, int(bits), _ptr(out), _stream()))
+    return out
+
+
+def qz_unpack(words, cols, bits):
+    torch = _torch()
+    _dev(words, "words")
+    rows = words.shape[0]
+    out = torch.empty((rows, cols), dtype=torch.uint8, device=words.device)
+    _check(lib().qz_unpack(_ptr(words), rows, cols, int(bits), _ptr(out), _stream()))
+    return out
+
+
+def qz_timing_enable(on=True):
+    _check(lib().qz_timing_enable(1 if on else 0))
+
+
+def qz_timing_read(reset=True):
+    """{kind name: (launches, total_ms)} of the launches recorded while timing was on."""
+    n = 16
+    launches = (C.c_int64 * n)()
+    total = (C.c_double * n)()
+    k = lib().qz_timing_read(launches, total, n, 1 if reset else 0)
+    if k < 0:
+        _check(k)
+    return {lib().qz_timing_kind_name(i).decode(): (launches[i], total[i]) for i in range(min(k, n))
+            if launches[i] > 0}
+
+
+def qz_last_error() -> str:
+    return lib().qz_last_error().decode(errors="replace")

@@ -1,0 +1,91 @@
+"""ctypes declarations of libqz (include/qz.h).  Loading fails loudly when the built
+library is missing: there is no fallback implementation."""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqz.so")
+
+QZ_OK, QZ_EINVAL, QZ_ENOTPD, QZ_ENONFINITE, QZ_EHIP, QZ_ESOLVER, QZ_EWORKSPACE = 0, -1, -2, -3, -4, -5, -6
+QZ_BF16, QZ_F32 = 0, 1
+QZ_GRID_CALLER = 0x1
+QZ_H_ACCUMULATE = 0x1
+QZ_H_NO_FINALIZE = 0x2
+QZ_ADMM_WARM_START = 0x1
+QZ_ADMM_REFRESH_UNCLAMPED = 0x2
+QZ_ADMM_REFRESH_FROM_Z = 0x4
+QZ_ADMM_DUAL_NO_RESCALE = 0x8
+
+STATUS_NAMES = {0: "QZ_OK", -1: "QZ_EINVAL", -2: "QZ_ENOTPD", -3: "QZ_ENONFINITE", -4: "QZ_EHIP",
+                -5: "QZ_ESOLVER", -6: "QZ_EWORKSPACE"}
+
+# every entry point declared in include/qz.h
+EXPORTS = ("qz_hessian_workspace", "qz_build_hessian", "qz_rtn", "qz_gptq_workspace", "qz_gptq",
+           "qz_admmq_prepare", "qz_admmq_workspace", "qz_admmq", "qz_packed_words", "qz_pack",
+           "qz_unpack", "qz_timing_enable", "qz_timing_read", "qz_timing_kind_name",
+           "qz_last_error", "qz_abi_version")
+
+
+class QzGrid(C.Structure):
+    _fields_ = [("struct_size", C.c_uint32), ("bits", C.c_int32), ("group_size", C.c_int32),
+                ("flags", C.c_uint32)]
+
+
+class QzAdmm(C.Structure):
+    _fields_ = [("struct_size", C.c_uint32), ("iters", C.c_int32), ("rho0", C.c_float),
+                ("gamma", C.c_float), ("refresh_every", C.c_int32), ("flags", C.c_uint32),
+                ("t0", C.c_int32)]
+
+
+P = C.c_void_p
+I64 = C.c_int64
+I32 = C.c_int32
+U32 = C.c_uint32
+SZ = C.c_size_t
+F = C.c_float
+
+_SIGS = {
+    "qz_hessian_workspace": (SZ, [I64, I64, I32]),
+    "qz_build_hessian": (C.c_int, [P, I32, I64, I64, F, U32, P, P, P, P, P, SZ, P]),
+    "qz_rtn": (C.c_int, [P, I32, I64, I64, C.POINTER(QzGrid), P, P, P, P]),
+    "qz_gptq_workspace": (SZ, [I64, I64, I32]),
+    "qz_gptq": (C.c_int, [P, P, I32, I64, I64, C.POINTER(QzGrid), I32, P, P, P, P, P, SZ, P]),
+    "qz_admmq_prepare": (C.c_int, [P, I64, P, P, P, P]),
+    "qz_admmq_workspace": (SZ, [I64, I64, I32, I32]),
+    "qz_admmq": (C.c_int, [P, P, P, P, I32, I64, I64, C.POINTER(QzGrid), C.POINTER(QzAdmm), P, P, P,
+                           P, P, P, SZ, P]),
+    "qz_packed_words": (I64, [I64, I32]),
+    "qz_pack": (C.c_int, [P, I64, I64, I32, P, P]),
+    "qz_unpack": (C.c_int, [P, I64, I64, I32, P, P]),
+    "qz_timing_enable": (C.c_int, [C.c_int]),
+    "qz_timing_read": (C.c_int, [C.POINTER(C.c_int64), C.POINTER(C.c_double), C.c_int, C.c_int]),
+    "qz_timing_kind_name": (C.c_char_p, [C.c_int]),
+    "qz_last_error": (C.c_char_p, []),
+    "qz_abi_version": (C.c_int, []),
+}
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libqz.so and declare its signatures.  Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libqz.so not found at {path}; build it with "
+                          f"`python -m post_weight_quantization_05_amd.build`")
+    # PyTorch ships its own HIP runtime and loads it by path.  Importing torch first
+    # makes libqz's libamdhip64.so.7 dependency resolve (by soname) to that same
+    # runtime, so device pointers and streams from torch are valid in libqz.  Loading
+    # libqz first would bring up a second, separate HIP runtime in the process.
+    import torch  # noqa: F401
+    lib = C.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib

@@ -1,0 +1,396 @@
+// C ABI of libqz (declared and documented in include/qz.h): argument checks,
+// workspace layout and the launch sequence of each solver.  Nothing here computes;
+// every step runs in the kernels of the k_*.hip translation units.
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "qz_internal.h"
+
+namespace qz {
+
+namespace {
+thread_local std::string g_err;
+
+constexpr int kMaxDevices = 64;
+std::mutex g_flag_mu;
+uint32_t* g_flag[kMaxDevices] = {};
+
+// A 4-byte status word per device for the entry points that take no workspace
+// (qz_rtn); allocated on first use and kept for the life of the process.
+int device_flag(uint32_t** out) {
+  int dev = 0;
+  QZ_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(QZ_EHIP, "device index out of range");
+  std::lock_guard<std::mutex> lk(g_flag_mu);
+  if (!g_flag[dev]) QZ_HIP(hipMalloc(&g_flag[dev], sizeof(uint32_t)));
+  *out = g_flag[dev];
+  return QZ_OK;
+}
+
+int read_flag(const uint32_t* flag, hipStream_t s, uint32_t* host) {
+  *host = 0;
+  QZ_HIP(hipMemcpyAsync(host, flag, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
+  QZ_HIP(hipStreamSynchronize(s));
+  return QZ_OK;
+}
+
+bool valid_dtype(int t) { return t == QZ_BF16 || t == QZ_F32; }
+
+int check_grid(const qz_grid* g, int64_t d_i) {
+  if (!g) return fail(QZ_EINVAL, "grid is null");
+  if (g->struct_size < sizeof(qz_grid)) return fail(QZ_EINVAL, "grid.struct_size too small");
+  if (g->bits < 2 || g->bits > 8) return fail(QZ_EINVAL, "grid.bits must be in 2..8");
+  if (g->group_size < 1) return fail(QZ_EINVAL, "grid.group_size must be >= 1");
+  if (d_i % g->group_size != 0) return fail(QZ_EINVAL, "grid.group_size must divide d_i");
+  if (g->flags & ~QZ_GRID_CALLER) return fail(QZ_EINVAL, "grid.flags has unknown bits");
+  return QZ_OK;
+}
+
+size_t gptq_ws(int64_t d_o, int64_t d_i) {
+  Carver c(nullptr);
+  c.take<uint32_t>(1);
+  c.take<float>(static_cast<size_t>(d_o) * round_up(d_i, 4));   // W working copy
+  c.take<float>(static_cast<size_t>(d_o) * 128);                 // E
+  c.take<float>(static_cast<size_t>(d_i) * round_up(d_i, 4));   // R^T
+  c.take<uint32_t>(static_cast<size_t>(d_i));                    // permutation check
+  c.used += rfactor_ws_bytes(d_i);
+  return c.used;
+}
+
+size_t admm_ws(int64_t d_o, int64_t d_i, int64_t group, int64_t iters) {
+  const int64_t ld = round_up(d_i, 4);
+  const int64_t G = group > 0 ? d_i / group : 0;
+  Carver c(nullptr);
+  c.take<uint32_t>(1);
+  c.take<float>(static_cast<size_t>(d_i) * ld);          // V^T
+  for (int i = 0; i < 4; ++i) c.take<float>(static_cast<size_t>(d_o) * ld);   // P, M, T, W~
+  c.take<float>(static_cast<size_t>(d_o) * d_i);         // U (when the caller passes none)
+  c.take<float>(static_cast<size_t>(d_o) * G);           // lo_0
+  c.take<float>(static_cast<size_t>(d_o) * G);           // hi_0
+  c.take<float>(static_cast<size_t>(d_o) * G);           // s_0 scratch
+  c.take<uint8_t>(static_cast<size_t>(d_o) * G);         // z_0 scratch
+  c.take<float>(static_cast<size_t>(d_i));               // 1 / sigma
+  c.take<double>(static_cast<size_t>(iters > 0 ? iters : 1) * admm_proj_blocks() * 2);
+  return c.used;
+}
+
+}  // namespace
+
+void set_error(const std::string& msg) { g_err = msg; }
+const char* last_error() { return g_err.c_str(); }
+int fail(int code, const std::string& msg) {
+  set_error(msg);
+  return code;
+}
+int check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(QZ_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+  return QZ_OK;
+}
+
+}  // namespace qz
+
+using namespace qz;
+
+extern "C" {
+
+const char* qz_last_error(void) { return qz::last_error(); }
+int qz_abi_version(void) { return QZ_ABI_VERSION; }
+
+// ------------------------------------------------------------------ Hessian
+size_t qz_hessian_workspace(int64_t n, int64_t d_i, int32_t xt) {
+  if (n < 0 || d_i < 1 || !valid_dtype(xt)) return 0;
+  return hessian_ws_bytes(n, d_i, xt);
+}
+
+int qz_build_hessian(const void* X, int32_t xt, int64_t n, int64_t d_i, float damp, uint32_t flags,
+                     float* H, float* diag, float* sigma, float* lambda_out, void* ws,
+                     size_t ws_bytes, hipStream_t stream) {
+  if (!valid_dtype(xt)) return fail(QZ_EINVAL, "build_hessian: bad dtype");
+  if (n < 0 || d_i < 1) return fail(QZ_EINVAL, "build_hessian: need n >= 0 and d_i >= 1");
+  if (!H || (n > 0 && !X)) return fail(QZ_EINVAL, "build_hessian: null pointer");
+  if (!(damp >= 0.f) || !std::isfinite(damp)) return fail(QZ_EINVAL, "build_hessian: damp must be finite and >= 0");
+  if (flags & ~(QZ_H_ACCUMULATE | QZ_H_NO_FINALIZE)) return fail(QZ_EINVAL, "build_hessian: unknown flags");
+  const size_t need = hessian_ws_bytes(n, d_i, xt);
+  if (ws_bytes < need || (need > 0 && !ws)) return fail(QZ_EWORKSPACE, "build_hessian: workspace too small");
+  set_error("");
+  return hessian_build(X, xt, n, d_i, damp, flags, H, diag, sigma, lambda_out, ws, ws_bytes, stream);
+}
+
+// ------------------------------------------------------------------ RTN
+int qz_rtn(const void* W, int32_t wt, int64_t d_o, int64_t d_i, const qz_grid* grid,
+           uint8_t* codes, float* scales, uint8_t* zeros, hipStream_t stream) {
+  if (!valid_dtype(wt)) return fail(QZ_EINVAL, "rtn: bad dtype");
+  if (d_o < 0 || d_i < 1) return fail(QZ_EINVAL, "rtn: need d_o >= 0 and d_i >= 1");
+  QZ_TRY(check_grid(grid, d_i));
+  if (d_o == 0) return QZ_OK;
+  if (!W || !codes || !scales || !zeros) return fail(QZ_EINVAL, "rtn: null pointer");
+  uint32_t* flag = nullptr;
+  QZ_TRY(device_flag(&flag));
+  QZ_TRY(launch_fill_u32(flag, 1, 0u, stream));
+  {
+    ScopedTimer tm(K_GRID_RTN, stream);
+    if (!(grid->flags & QZ_GRID_CALLER)) {
+      QZ_TRY(launch_grid_fit(W, wt, d_o, d_i, grid->group_size, grid->bits, scales, zeros, nullptr,
+                             nullptr, flag, stream));
+    }
+    QZ_TRY(launch_rtn(W, wt, d_o, d_i, grid->group_size, grid->bits, scales, zeros, codes, stream));
+  }
+  uint32_t h = 0;
+  QZ_TRY(read_flag(flag, stream, &h));
+  if (h & FLAG_NONFINITE) return fail(QZ_ENONFINITE, "rtn: non-finite weight");
+  return QZ_OK;
+}
+
+// ------------------------------------------------------------------ GPTQ
+size_t qz_gptq_workspace(int64_t d_o, int64_t d_i, int32_t B) {
+  if (d_o < 0 || d_i < 1 || B < 1 || B > 128) return 0;
+  return gptq_ws(d_o, d_i);
+}
+
+int qz_gptq(const float* H, const void* W_hat, int32_t wt, int64_t d_o, int64_t d_i,
+            const qz_grid* grid, int32_t B, const int32_t* perm, uint8_t* codes, float* scales,
+            uint8_t* zeros, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!valid_dtype(wt)) return fail(QZ_EINVAL, "gptq: bad dtype");
+  if (d_o < 0 || d_i < 1) return fail(QZ_EINVAL, "gptq: need d_o >= 0 and d_i >= 1");
+  if (B < 1 || B > 128) return fail(QZ_EINVAL, "gptq: block size B must be in 1..128");
+  QZ_TRY(check_grid(grid, d_i));
+  if (!H || (d_o > 0 && (!W_hat || !codes || !scales || !zeros)))
+    return fail(QZ_EINVAL, "gptq: null pointer");
+  const size_t need = gptq_ws(d_o, d_i);
+  if (ws_bytes < need || !ws) return fail(QZ_EWORKSPACE, "gptq: workspace too small");
+  set_error("");
+
+  const int64_t ldw = round_up(d_i, 4), lde = 128, ldr = round_up(d_i, 4);
+  const int64_t G = d_i / grid->group_size;
+  Carver cv(ws);
+  uint32_t* flag = cv.take<uint32_t>(1);
+  float* Wf = cv.take<float>(static_cast<size_t>(d_o) * ldw);
+  float* E = cv.take<float>(static_cast<size_t>(d_o) * lde);
+  float* Rt = cv.take<float>(static_cast<size_t>(d_i) * ldr);
+  uint32_t* counts = cv.take<uint32_t>(static_cast<size_t>(d_i));
+  void* rws = cv.base + cv.used;
+
+  QZ_TRY(launch_fill_u32(flag, 1, 0u, stream));
+  if (perm) {
+    // every later kernel indexes through perm: validate it first
+    QZ_TRY(launch_check_perm(perm, d_i, counts, flag, stream));
+    uint32_t hp = 0;
+    QZ_TRY(read_flag(flag, stream, &hp));
+    if (hp & FLAG_BADARG) return fail(QZ_EINVAL, "gptq: perm is not a permutation of 0..d_i-1");
+  }
+  if (d_o > 0) {
+    ScopedTimer tm(K_GRID_RTN, stream);
+    if (!(grid->flags & QZ_GRID_CALLER))
+      QZ_TRY(launch_grid_fit(W_hat, wt, d_o, d_i, grid->group_size, grid->bits, scales, zeros,
+                             nullptr, nullptr, flag, stream));
+    QZ_TRY(launch_to_f32(W_hat, wt, d_o, d_i, perm, nullptr, Wf, ldw, flag, stream));
+  }
+  {
+    ScopedTimer tm(K_RFACTOR, stream);
+    QZ_TRY(rfactor(H, d_i, perm, Rt, ldr, rws, flag, stream));
+  }
+  uint32_t h = 0;
+  QZ_TRY(read_flag(flag, stream, &h));
+  if (h & FLAG_NONFINITE) return fail(QZ_ENONFINITE, "gptq: non-finite H or W_hat");
+  if (h & FLAG_NOTPD) return fail(QZ_ENOTPD, "gptq: H is not positive definite (increase damping)");
+  if (d_o == 0) return QZ_OK;
+
+  for (int64_t a = 0; a < d_i; a += B) {
+    const int64_t b = (a + B < d_i) ? a + B : d_i;
+    {
+      ScopedTimer tm(K_GPTQ_BLOCK, stream);
+      QZ_TRY(launch_gptq_block(Wf, ldw, d_o, a, b, Rt, ldr, scales, zeros, G, grid->group_size,
+                               grid->bits, perm, E, lde, codes, d_i, stream));
+    }
+    if (b < d_i) {
+      GemmArgs g{};
+      g.M = d_o;
+      g.N = d_i - b;
+      g.K = b - a;
+      g.A = E;
+      g.lda = lde;
+      g.B = Rt + b * ldr + a;   // row b+n, columns a.. : R[a+k][b+n]
+      g.ldb = ldr;
+      g.C = Wf + b;
+      g.ldc = ldw;
+      ScopedTimer tm(K_GEMM_GPTQ, stream);
+      QZ_TRY(launch_gemm_nt(EPI_SUB, g, stream));
+    }
+  }
+  return QZ_OK;
+}
+
+// ------------------------------------------------------------------ ADMM-Q
+int qz_admmq_prepare(const float* H, int64_t d_i, float* V, float* Lambda, float* sigma,
+                     hipStream_t stream) {
+  if (d_i < 1) return fail(QZ_EINVAL, "admmq_prepare: d_i must be >= 1");
+  if (!H || !V || !Lambda || !sigma) return fail(QZ_EINVAL, "admmq_prepare: null pointer");
+  set_error("");
+  ScopedTimer tm(K_EIG, stream);
+  return eig_scaled(H, d_i, V, Lambda, sigma, stream);
+}
+
+size_t qz_admmq_workspace(int64_t d_o, int64_t d_i, int32_t group_size, int32_t iters) {
+  if (d_o < 0 || d_i < 1 || group_size < 1 || d_i % group_size || iters < 0) return 0;
+  return admm_ws(d_o, d_i, group_size, iters);
+}
+
+int qz_admmq(const float* V, const float* Lambda, const float* sigma, const void* W_hat, int32_t wt,
+             int64_t d_o, int64_t d_i, const qz_grid* grid, const qz_admm* p, uint8_t* codes,
+             float* scales, uint8_t* zeros, float* U, float* residuals, void* ws, size_t ws_bytes,
+             hipStream_t stream) {
+  if (!valid_dtype(wt)) return fail(QZ_EINVAL, "admmq: bad dtype");
+  if (d_o < 0 || d_i < 1) return fail(QZ_EINVAL, "admmq: need d_o >= 0 and d_i >= 1");
+  QZ_TRY(check_grid(grid, d_i));
+  if (!p || p->struct_size < sizeof(qz_admm)) return fail(QZ_EINVAL, "admmq: params null or struct_size too small");
+  const uint32_t known = QZ_ADMM_WARM_START | QZ_ADMM_REFRESH_UNCLAMPED | QZ_ADMM_REFRESH_FROM_Z |
+                         QZ_ADMM_DUAL_NO_RESCALE;
+  if (p->flags & ~known) return fail(QZ_EINVAL, "admmq: unknown flags");
+  if ((p->flags & QZ_ADMM_REFRESH_UNCLAMPED) && (p->flags & QZ_ADMM_REFRESH_FROM_Z))
+    return fail(QZ_EINVAL, "admmq: REFRESH_UNCLAMPED and REFRESH_FROM_Z are exclusive");
+  if (p->iters < 0 || p->refresh_every < 0 || p->t0 < 0) return fail(QZ_EINVAL, "admmq: negative count");
+  if (!(p->rho0 > 0.f) || !(p->gamma > 0.f) || !std::isfinite(p->rho0) || !std::isfinite(p->gamma))
+    return fail(QZ_EINVAL, "admmq: rho0 and gamma must be finite and > 0");
+  const bool warm = p->flags & QZ_ADMM_WARM_START;
+  const bool caller_grid = grid->flags & QZ_GRID_CALLER;
+  if (warm && !U) return fail(QZ_EINVAL, "admmq: WARM_START needs U");
+  if (warm && caller_grid && p->refresh_every > 0)
+    return fail(QZ_EINVAL, "admmq: WARM_START with a caller grid and refresh is not supported");
+  if (!V || !Lambda || !sigma || (d_o > 0 && (!W_hat || !codes || !scales || !zeros)))
+    return fail(QZ_EINVAL, "admmq: null pointer");
+  const size_t need = admm_ws(d_o, d_i, grid->group_size, p->iters);
+  if (ws_bytes < need || !ws) return fail(QZ_EWORKSPACE, "admmq: workspace too small");
+  set_error("");
+  if (d_o == 0) return QZ_OK;
+
+  const int group = grid->group_size, bits = grid->bits;
+  const int64_t ld = round_up(d_i, 4);
+  const int64_t G = d_i / group;
+  const int nblk = admm_proj_blocks();
+  Carver cv(ws);
+  uint32_t* flag = cv.take<uint32_t>(1);
+  float* Vt = cv.take<float>(static_cast<size_t>(d_i) * ld);
+  float* P = cv.take<float>(static_cast<size_t>(d_o) * ld);
+  float* M = cv.take<float>(static_cast<size_t>(d_o) * ld);
+  float* T = cv.take<float>(static_cast<size_t>(d_o) * ld);
+  float* Wt = cv.take<float>(static_cast<size_t>(d_o) * ld);
+  float* Uws = cv.take<float>(static_cast<size_t>(d_o) * d_i);
+  float* lo0 = cv.take<float>(static_cast<size_t>(d_o) * G);
+  float* hi0 = cv.take<float>(static_cast<size_t>(d_o) * G);
+  float* s0 = cv.take<float>(static_cast<size_t>(d_o) * G);
+  uint8_t* z0 = cv.take<uint8_t>(static_cast<size_t>(d_o) * G);
+  float* inv_sigma = cv.take<float>(static_cast<size_t>(d_i));
+  double* partial = cv.take<double>(static_cast<size_t>(p->iters > 0 ? p->iters : 1) * nblk * 2);
+  float* Ub = U ? U : Uws;
+
+  QZ_TRY(launch_fill_u32(flag, 1, 0u, stream));
+  QZ_TRY(launch_inverse_f32(sigma, d_i, inv_sigma, stream));
+  QZ_TRY(launch_transpose_f32(V, d_i, d_i, d_i, Vt, ld, stream));
+  // the static grid of W_hat: its range [lo_0, hi_0] bounds the refresh
+  if (!caller_grid) {
+    if (warm)
+      QZ_TRY(launch_grid_fit(W_hat, wt, d_o, d_i, group, bits, s0, z0, lo0, hi0, flag, stream));
+    else
+      QZ_TRY(launch_grid_fit(W_hat, wt, d_o, d_i, group, bits, scales, zeros, lo0, hi0, flag, stream));
+  } else {
+    QZ_TRY(launch_range_of_grid(scales, zeros, d_o * G, bits, lo0, hi0, stream));
+  }
+  // P = W~_hat V Lambda with W~_hat = W_hat / Sigma (staged in T)
+  QZ_TRY(launch_to_f32(W_hat, wt, d_o, d_i, nullptr, sigma, T, ld, flag, stream));
+  {
+    GemmArgs g{};
+    g.M = d_o; g.N = d_i; g.K = d_i;
+    g.A = T; g.lda = ld;
+    g.B = Vt; g.ldb = ld;
+    g.C = P; g.ldc = ld;
+    g.colv = Lambda;
+    ScopedTimer tm(K_GEMM_ADMM_SETUP, stream);
+    QZ_TRY(launch_gemm_nt(EPI_COLSCALE, g, stream));
+  }
+  if (!warm) {
+    QZ_TRY(launch_rtn(W_hat, wt, d_o, d_i, group, bits, scales, zeros, codes, stream));
+    QZ_TRY(launch_fill_f32(Ub, d_o * d_i, 0.f, stream));
+  }
+  QZ_TRY(launch_admm_init_m(codes, scales, zeros, Ub, inv_sigma, d_o, d_i, group, M, ld, stream));
+
+  int refresh_mode = 1;
+  if (p->flags & QZ_ADMM_REFRESH_UNCLAMPED) refresh_mode = 2;
+  if (p->flags & QZ_ADMM_REFRESH_FROM_Z) refresh_mode = 3;
+  const int t0 = warm ? p->t0 : 0;
+  for (int k = 0; k < p->iters; ++k) {
+    const int t = t0 + k;
+    const double rho = static_cast<double>(p->rho0) * std::pow(static_cast<double>(p->gamma), t);
+    const double rho_next = rho * static_cast<double>(p->gamma);
+    GemmArgs g1{};
+    g1.M = d_o; g1.N = d_i; g1.K = d_i;
+    g1.A = M; g1.lda = ld;
+    g1.B = Vt; g1.ldb = ld;
+    g1.C = T; g1.ldc = ld;
+    g1.P = P; g1.ldp = ld;
+    g1.colv = Lambda;
+    g1.rho = static_cast<float>(rho);
+    {
+      ScopedTimer tm(K_GEMM_ADMM1, stream);
+      QZ_TRY(launch_gemm_nt(EPI_ADMM1, g1, stream));
+    }
+    GemmArgs g2{};
+    g2.M = d_o; g2.N = d_i; g2.K = d_i;
+    g2.A = T; g2.lda = ld;
+    g2.B = V; g2.ldb = d_i;
+    g2.C = Wt; g2.ldc = ld;
+    {
+      ScopedTimer tm(K_GEMM_ADMM2, stream);
+      QZ_TRY(launch_gemm_nt(EPI_STORE, g2, stream));
+    }
+    AdmmProj pr{};
+    pr.Wt = Wt; pr.ldw = ld;
+    pr.U = Ub;
+    pr.M = M; pr.ldm = ld;
+    pr.codes = codes;
+    pr.scales = scales; pr.zeros = zeros;
+    pr.lo0 = lo0; pr.hi0 = hi0;
+    pr.sigma = sigma;
+    pr.d_o = d_o; pr.d_i = d_i; pr.group = group; pr.bits = bits;
+    pr.rho = static_cast<float>(rho);
+    pr.rho_next = static_cast<float>(rho_next);
+    pr.refresh = (p->refresh_every > 0 && t % p->refresh_every == 0) ? refresh_mode : 0;
+    pr.rescale = (p->flags & QZ_ADMM_DUAL_NO_RESCALE) ? 0 : 1;
+    pr.partial = partial + static_cast<int64_t>(k) * nblk * 2;
+    ScopedTimer tm(K_ADMM_PROJECT, stream);
+    QZ_TRY(launch_admm_project(pr, stream, inv_sigma));
+  }
+  QZ_TRY(launch_admm_residuals(partial, p->iters, nblk, residuals, flag, stream));
+  uint32_t h = 0;
+  QZ_TRY(read_flag(flag, stream, &h));
+  if (h & FLAG_NONFINITE) return fail(QZ_ENONFINITE, "admmq: non-finite W_hat or iterate");
+  return QZ_OK;
+}
+
+// ------------------------------------------------------------------ packing
+int64_t qz_packed_words(int64_t cols, int32_t bits) {
+  if (cols < 0 || bits < 1 || bits > 8) return -1;
+  return ceil_div(cols * bits, 32);
+}
+
+int qz_pack(const uint8_t* codes, int64_t rows, int64_t cols, int32_t bits, uint32_t* out,
+            hipStream_t stream) {
+  if (rows < 0 || cols < 0 || bits < 1 || bits > 8) return fail(QZ_EINVAL, "pack: bad size or bits");
+  if (rows * cols > 0 && (!codes || !out)) return fail(QZ_EINVAL, "pack: null pointer");
+  set_error("");
+  ScopedTimer tm(K_PACK, stream);
+  return launch_pack(codes, rows, cols, bits, out, stream);
+}
+
+int qz_unpack(const uint32_t* in, int64_t rows, int64_t cols, int32_t bits, uint8_t* codes,
+              hipStream_t stream) {
+  if (rows < 0 || cols < 0 || bits < 1 || bits > 8) return fail(QZ_EINVAL, "unpack: bad size or bits");
+  if (rows * cols > 0 && (!codes || !in)) return fail(QZ_EINVAL, "unpack: null pointer");
+  set_error("");
+  ScopedTimer tm(K_PACK, stream);
+  return launch_unpack(in, rows, cols, bits, codes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,267 @@
+// ADMM-Q streaming kernels (ADMM-Q summary, 2. key algorithmic components).
+//
+// admm_project fuses, per iteration, everything after the W-update into one pass
+// over the weights, one wavefront per (row, group):
+//   grid refresh   -- scale and zero refit from min/max of the continuous iterate
+//                     (W~ Sigma), range forced to hold 0 and, by default, clamped
+//                     into the group's initial range [lo_0, hi_0];
+//   D-update       -- C = clamp(rint((W~ + U) Sigma / s) + z): the projection onto the
+//                     grid is round-to-nearest in original coordinates;
+//                     D~ = s (C - z) / Sigma;
+//   dual update    -- U = (U + W~ - D~) * rho_t / rho_{t+1} (multiplier kept across the
+//                     penalty schedule rho_t = rho_0 gamma^t);
+//   next input     -- M = D~ - U for the next W-update;
+//   residuals      -- sum (W~ - D~)^2 and rho_t^2 sum (D~ - D~_prev)^2, reduced per
+//                     workgroup in fp64 into a per-iteration partial slot.
+// It reads W~, U (fp32) and the previous codes (u8) and writes U, M (fp32) and the
+// codes: 18 bytes per weight, the whole iteration's HBM traffic outside the GEMMs.
+#include "qz_internal.h"
+
+// No fused multiply-add contraction in this file: D~ = s (C - z) / Sigma and M = D~ - U
+// are rounded exactly as written, so a run resumed from its saved state (codes, grid,
+// U) rebuilds M bit for bit.
+#pragma clang fp contract(off)
+
+namespace qz {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kProjBlocks = 2048;
+
+__global__ __launch_bounds__(kThreads) void project_kernel(const AdmmProj p,
+                                                           const float* __restrict__ inv_sigma) {
+  __shared__ double red[kThreads / 64][2];
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int64_t G = p.d_i / p.group;
+  const int64_t total = p.d_o * G;
+  const float maxq = static_cast<float>((1 << p.bits) - 1);
+  const int64_t wpb = kThreads / 64;
+  double acc_p = 0.0, acc_d = 0.0;
+
+  for (int64_t t = blockIdx.x * wpb + wid; t < total; t += static_cast<int64_t>(gridDim.x) * wpb) {
+    const int64_t r = t / G, g = t % G;
+    const int64_t c0 = g * p.group;
+    const float* wt = p.Wt + r * p.ldw + c0;
+    float* u = p.U + r * p.d_i + c0;
+    float* m = p.M + r * p.ldm + c0;
+    uint8_t* cd = p.codes + r * p.d_i + c0;
+    const float* sg = p.sigma + c0;
+    const float* isg = inv_sigma + c0;
+
+    const float s_old = p.scales[t];
+    const float z_old = static_cast<float>(p.zeros[t]);
+    float s = s_old, z = z_old;
+    if (p.refresh) {
+      float lo = 0.f, hi = 0.f;
+      for (int i = lane; i < p.group; i += 64) {
+        float v = wt[i];
+        if (p.refresh == 3) v += u[i];
+        v *= sg[i];
+        lo = fminf(lo, v);
+        hi = fmaxf(hi, v);
+      }
+      for (int off = 32; off > 0; off >>= 1) {
+        lo = fminf(lo, __shfl_xor(lo, off));
+        hi = fmaxf(hi, __shfl_xor(hi, off));
+      }
+      if (hi == lo) { lo = -1.f; hi = 1.f; }
+      if (p.refresh != 2) {
+        lo = fmaxf(lo, p.lo0[t]);
+        hi = fminf(hi, p.hi0[t]);
+      }
+      s = (hi - lo) / maxq;
+      z = fminf(fmaxf(__builtin_rintf(-lo / s), 0.f), maxq);
+    }
+    const float rs = p.rescale ? p.rho / p.rho_next : 1.0f;
+    for (int i = lane; i < p.group; i += 64) {
+      const float w = wt[i];
+      const float uu = u[i];
+      const float zv = (w + uu) * sg[i];
+      const float c = quant_code(zv, s, z, maxq);
+      const float dt = s * (c - z) * isg[i];
+      const float dold = s_old * (static_cast<float>(cd[i]) - z_old) * isg[i];
+      const float un = (uu + w - dt) * rs;
+      u[i] = un;
+      m[i] = dt - un;
+      cd[i] = static_cast<uint8_t>(c);
+      const float ep = w - dt, ed = dt - dold;
+      acc_p += static_cast<double>(ep) * ep;
+      acc_d += static_cast<double>(ed) * ed;
+    }
+    if (p.refresh && lane == 0) {
+      p.scales[t] = s;
+      p.zeros[t] = static_cast<uint8_t>(z);
+    }
+  }
+  // wavefront then workgroup reduction (fixed order)
+  for (int off = 32; off > 0; off >>= 1) {
+    acc_p += __shfl_xor(acc_p, off);
+    acc_d += __shfl_xor(acc_d, off);
+  }
+  if (lane == 0) {
+    red[wid][0] = acc_p;
+    red[wid][1] = acc_d;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double sp = 0.0, sd = 0.0;
+    for (int w = 0; w < kThreads / 64; ++w) {
+      sp += red[w][0];
+      sd += red[w][1];
+    }
+    const double rho = p.rho;
+    p.partial[2 * blockIdx.x] = sp;
+    p.partial[2 * blockIdx.x + 1] = rho * rho * sd;
+  }
+}
+
+// M = s (C - z) / Sigma - U  (U may be null: zero)
+__global__ __launch_bounds__(kThreads) void init_m_kernel(const uint8_t* __restrict__ codes,
+                                                          const float* __restrict__ scales,
+                                                          const uint8_t* __restrict__ zeros,
+                                                          const float* __restrict__ U,
+                                                          const float* __restrict__ inv_sigma,
+                                                          int64_t d_o, int64_t d_i, int group,
+                                                          float* __restrict__ M, int64_t ldm) {
+  const int64_t G = d_i / group;
+  const int64_t total = d_o * d_i;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = e / d_i, j = e % d_i;
+    const int64_t gi = r * G + j / group;
+    const float dt = scales[gi] * (static_cast<float>(codes[e]) - static_cast<float>(zeros[gi])) *
+                     inv_sigma[j];
+    M[r * ldm + j] = dt - (U ? U[e] : 0.f);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void residual_kernel(const double* __restrict__ partial,
+                                                            int iters, int nblocks,
+                                                            float* __restrict__ residuals,
+                                                            uint32_t* __restrict__ flag) {
+  for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < iters; t += gridDim.x * blockDim.x) {
+    double sp = 0.0, sd = 0.0;
+    const double* q = partial + static_cast<int64_t>(t) * nblocks * 2;
+    for (int b = 0; b < nblocks; ++b) {
+      sp += q[2 * b];
+      sd += q[2 * b + 1];
+    }
+    const float rp = static_cast<float>(sqrt(sp)), rd = static_cast<float>(sqrt(sd));
+    if (residuals) {
+      residuals[2 * t] = rp;
+      residuals[2 * t + 1] = rd;
+    }
+    if (!__builtin_isfinite(rp) || !__builtin_isfinite(rd)) atomicOr(flag, FLAG_NONFINITE);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void fill_kernel(float* __restrict__ p, int64_t n, float v) {
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n;
+       e += (int64_t)gridDim.x * blockDim.x)
+    p[e] = v;
+}
+
+__global__ __launch_bounds__(kThreads) void inv_kernel(const float* __restrict__ x, int64_t n,
+                                                       float* __restrict__ y) {
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n;
+       e += (int64_t)gridDim.x * blockDim.x)
+    y[e] = 1.0f / x[e];
+}
+
+// lo_0 = s (0 - z), hi_0 = s (2^b - 1 - z) for a caller-supplied grid.
+__global__ __launch_bounds__(kThreads) void range_of_grid_kernel(const float* __restrict__ scales,
+                                                                 const uint8_t* __restrict__ zeros,
+                                                                 int64_t n, float maxq,
+                                                                 float* __restrict__ lo0,
+                                                                 float* __restrict__ hi0) {
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const float s = scales[e], z = static_cast<float>(zeros[e]);
+    lo0[e] = -s * z;
+    hi0[e] = s * (maxq - z);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void fill_u32_kernel(uint32_t* __restrict__ p, int64_t n,
+                                                            uint32_t v) {
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n;
+       e += (int64_t)gridDim.x * blockDim.x)
+    p[e] = v;
+}
+
+__global__ __launch_bounds__(kThreads) void copy_bytes_kernel(const uint8_t* __restrict__ src,
+                                                              int64_t n, uint8_t* __restrict__ dst) {
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n;
+       e += (int64_t)gridDim.x * blockDim.x)
+    dst[e] = src[e];
+}
+
+inline unsigned grid_for(int64_t n) {
+  int64_t b = ceil_div(n, kThreads * 4);
+  if (b > 65536) b = 65536;
+  if (b < 1) b = 1;
+  return static_cast<unsigned>(b);
+}
+
+}  // namespace
+
+int admm_proj_blocks() { return kProjBlocks; }
+
+int launch_admm_project(const AdmmProj& p, hipStream_t s, const float* inv_sigma) {
+  project_kernel<<<kProjBlocks, kThreads, 0, s>>>(p, inv_sigma);
+  return check_launch("admm_project");
+}
+
+int launch_admm_init_m(const uint8_t* codes, const float* scales, const uint8_t* zeros,
+                       const float* U, const float* inv_sigma, int64_t d_o, int64_t d_i, int group,
+                       float* M, int64_t ldm, hipStream_t s) {
+  if (d_o * d_i == 0) return QZ_OK;
+  init_m_kernel<<<grid_for(d_o * d_i), kThreads, 0, s>>>(codes, scales, zeros, U, inv_sigma, d_o,
+                                                          d_i, group, M, ldm);
+  return check_launch("admm_init_m");
+}
+
+int launch_admm_residuals(const double* partial, int iters, int nblocks, float* residuals,
+                          uint32_t* flag, hipStream_t s) {
+  if (iters <= 0) return QZ_OK;
+  residual_kernel<<<static_cast<unsigned>(ceil_div(iters, kThreads)), kThreads, 0, s>>>(
+      partial, iters, nblocks, residuals, flag);
+  return check_launch("admm_residuals");
+}
+
+int launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {
+  if (n == 0) return QZ_OK;
+  fill_kernel<<<grid_for(n), kThreads, 0, s>>>(p, n, v);
+  return check_launch("fill_f32");
+}
+
+int launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s) {
+  if (n == 0) return QZ_OK;
+  fill_u32_kernel<<<grid_for(n), kThreads, 0, s>>>(p, n, v);
+  return check_launch("fill_u32");
+}
+
+int launch_inverse_f32(const float* x, int64_t n, float* y, hipStream_t s) {
+  if (n == 0) return QZ_OK;
+  inv_kernel<<<grid_for(n), kThreads, 0, s>>>(x, n, y);
+  return check_launch("inverse_f32");
+}
+
+int launch_range_of_grid(const float* scales, const uint8_t* zeros, int64_t n, int bits,
+                         float* lo0, float* hi0, hipStream_t s) {
+  if (n == 0) return QZ_OK;
+  range_of_grid_kernel<<<grid_for(n), kThreads, 0, s>>>(scales, zeros, n,
+                                                         static_cast<float>((1 << bits) - 1), lo0, hi0);
+  return check_launch("range_of_grid");
+}
+
+int launch_copy_bytes(const void* src, int64_t n, void* dst, hipStream_t s) {
+  if (n == 0) return QZ_OK;
+  copy_bytes_kernel<<<grid_for(n), kThreads, 0, s>>>(static_cast<const uint8_t*>(src), n,
+                                                      static_cast<uint8_t*>(dst));
+  return check_launch("copy_bytes");
+}
+
+}  // namespace qz

@@ -1,0 +1,307 @@
+// Inverse Cholesky factor for GPTQ: upper-triangular R with R^T R = H^{-1}
+// (GPTQ tutorial, section 3: the algorithm runs on the upper Cholesky factor of the
+// damped inverse curvature, chosen over repeated inverse updates for stability).
+//
+// Route (no explicit inverse of H): with J the reversal permutation, factor the
+// reversed matrix J H J = L L^T (lower Cholesky); then H = (J L J)(J L J)^T with
+// J L J upper triangular, so H^{-1} = ((J L J)^{-1})^T (J L J)^{-1} and
+// R = (J L J)^{-1} = J L^{-1} J.  Both steps are blocked right-looking fp64 algorithms
+// on 64 x 64 tiles:
+//   Cholesky   -- per block column: factor + invert the diagonal block (one
+//                 workgroup, in LDS), scale the panel below by the inverse, update
+//                 the trailing lower triangle (tile GEMMs);
+//   inverse    -- X = L^{-1} by block forward substitution, S <- I: per block row i,
+//                 X[i, :i] = L_ii^{-1} S[i, :i], then S[r, :i] -= L[r, i] X[i, :i] for
+//                 the rows below (tile GEMMs).
+// The matrix is padded to a multiple of 64 with an identity block, which keeps every
+// tile full.  A pivot <= 1e-12 of its original diagonal entry (or not finite) sets
+// the not-positive-definite flag; the caller reads it at its sync point (the GPTQ
+// tutorial's damping section: a failed factorisation means more damping is needed).
+// Output: R^T (lower, row-major) in fp32, the layout the GPTQ kernels read.
+#include "qz_internal.h"
+
+namespace qz {
+
+namespace {
+
+constexpr int NB = 64;
+constexpr int kThreads = 256;
+
+// A[i][j] = Hp[d-1-i][d-1-j] (Hp = H[perm][:, perm]) for i, j < d; identity padding.
+__global__ __launch_bounds__(kThreads) void init_reversed(const float* __restrict__ H, int64_t d,
+                                                          const int32_t* __restrict__ perm,
+                                                          double* __restrict__ A, int64_t lda,
+                                                          double* __restrict__ diag0,
+                                                          uint32_t* __restrict__ flag) {
+  const int64_t total = lda * lda;
+  bool bad = false;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i = e / lda, j = e % lda;
+    double v;
+    if (i < d && j < d) {
+      int64_t si = d - 1 - i, sj = d - 1 - j;
+      if (perm) { si = perm[si]; sj = perm[sj]; }
+      const float h = H[si * d + sj];
+      bad |= !__builtin_isfinite(h);
+      v = static_cast<double>(h);
+    } else {
+      v = (i == j) ? 1.0 : 0.0;
+    }
+    A[e] = v;
+    if (i == j) diag0[i] = v;
+  }
+  if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(flag, FLAG_NONFINITE);
+}
+
+// Factor diagonal block k in place (lower) and write its inverse to Dinv[k].
+__global__ __launch_bounds__(kThreads) void diag_block(double* __restrict__ A, int64_t lda, int64_t k,
+                                                       const double* __restrict__ diag0,
+                                                       double* __restrict__ Dinv,
+                                                       uint32_t* __restrict__ flag) {
+  __shared__ double a[NB][NB + 1];
+  __shared__ double x[NB][NB + 1];
+  const int tid = threadIdx.x;
+  const int64_t k0 = k * NB;
+  for (int e = tid; e < NB * NB; e += kThreads) {
+    const int i = e / NB, j = e % NB;
+    a[i][j] = A[(k0 + i) * lda + k0 + j];
+    x[i][j] = (i == j) ? 1.0 : 0.0;
+  }
+  __syncthreads();
+  bool notpd = false;
+  // unblocked right-looking Cholesky of the lower triangle
+  for (int j = 0; j < NB; ++j) {
+    const double p = a[j][j];
+    const double tol = 1e-12 * diag0[k0 + j];
+    if (!(p > tol) || !__builtin_isfinite(p)) notpd = true;
+    const double ljj = sqrt(p > 0.0 ? p : 0.0);
+    __syncthreads();
+    if (tid == 0) a[j][j] = ljj;
+    for (int i = j + 1 + tid; i < NB; i += kThreads) a[i][j] = a[i][j] / ljj;
+    __syncthreads();
+    // trailing update a[i][l] -= a[i][j] a[l][j], j < l <= i
+    const int m = NB - j - 1;
+    for (int e = tid; e < m * m; e += kThreads) {
+      const int i = j + 1 + e / m, l = j + 1 + e % m;
+      if (l <= i) a[i][l] -= a[i][j] * a[l][j];
+    }
+    __syncthreads();
+  }
+  if (notpd && tid == 0) atomicOr(flag, FLAG_NOTPD);
+  // inverse of the lower factor by forward substitution on all columns at once:
+  // row i of X = (row i of B - sum_{p<i} L[i][p] X[p]) / L[i][i], done right-looking.
+  for (int i = 0; i < NB; ++i) {
+    const double inv = 1.0 / a[i][i];
+    for (int c = tid; c <= i; c += kThreads) x[i][c] *= inv;
+    __syncthreads();
+    const int m = NB - i - 1;
+    for (int e = tid; e < m * (i + 1); e += kThreads) {
+      const int r = i + 1 + e / (i + 1), c = e % (i + 1);
+      x[r][c] -= a[r][i] * x[i][c];
+    }
+    __syncthreads();
+  }
+  for (int e = tid; e < NB * NB; e += kThreads) {
+    const int i = e / NB, j = e % NB;
+    if (j <= i) A[(k0 + i) * lda + k0 + j] = a[i][j];
+    Dinv[k * NB * NB + e] = (j <= i) ? x[i][j] : 0.0;
+  }
+}
+
+// Rows below block k:  A[i][k-block] <- A[i][k-block] * Dinv_k^T.  One 64-row tile
+// per workgroup.
+__global__ __launch_bounds__(kThreads) void panel_solve(double* __restrict__ A, int64_t lda, int64_t k,
+                                                        const double* __restrict__ Dinv) {
+  __shared__ double p[NB][NB + 1];
+  __shared__ double dv[NB][NB + 1];
+  const int tid = threadIdx.x;
+  const int64_t k0 = k * NB;
+  const int64_t r0 = k0 + NB + static_cast<int64_t>(blockIdx.x) * NB;
+  for (int e = tid; e < NB * NB; e += kThreads) {
+    const int i = e / NB, j = e % NB;
+    p[i][j] = A[(r0 + i) * lda + k0 + j];
+    dv[i][j] = Dinv[k * NB * NB + e];
+  }
+  __syncthreads();
+  // out[i][c] = sum_{q <= c} p[i][q] * Dinv[c][q]
+  for (int e = tid; e < NB * NB; e += kThreads) {
+    const int i = e / NB, c = e % NB;
+    double s = 0.0;
+    for (int q = 0; q <= c; ++q) s += p[i][q] * dv[c][q];
+    A[(r0 + i) * lda + k0 + c] = s;
+  }
+}
+
+__device__ __forceinline__ void tri_tile(int64_t t, int64_t& ti, int64_t& tj) {
+  // lower-triangle enumeration: (0,0), (1,0), (1,1), (2,0), ...
+  int64_t i = static_cast<int64_t>((sqrt(8.0 * static_cast<double>(t) + 1.0) - 1.0) * 0.5);
+  while (i * (i + 1) / 2 > t) --i;
+  while ((i + 1) * (i + 2) / 2 <= t) ++i;
+  ti = i;
+  tj = t - i * (i + 1) / 2;
+}
+
+// C[64x64 tile] -= A_op * B_op with K = 64.
+//  A_op[m][q] = A[(am0 + m) * lda + ak0 + q]
+//  B_op[q][n] = BNN ? B[(bk0 + q) * ldb + bn0 + n] : B[(bn0 + n) * ldb + bk0 + q]
+// Threads own 4 x 4 outputs (rows ty + 16a, cols tx + 16b).
+template <bool BNN>
+__device__ __forceinline__ void tile_update(double* __restrict__ C, int64_t ldc, int64_t cm0,
+                                            int64_t cn0, const double* __restrict__ A, int64_t lda,
+                                            int64_t am0, int64_t ak0, const double* __restrict__ B,
+                                            int64_t ldb, int64_t bk0, int64_t bn0) {
+  __shared__ double as[NB][NB + 1];   // [q][m]
+  __shared__ double bs[NB][NB + 1];   // [q][n]
+  const int tid = threadIdx.x;
+  for (int e = tid; e < NB * NB; e += kThreads) {
+    const int r = e / NB, c = e % NB;
+    as[c][r] = A[(am0 + r) * lda + ak0 + c];              // A row r, k = c
+    if (BNN) bs[r][c] = B[(bk0 + r) * ldb + bn0 + c];     // k = r, n = c
+    else bs[c][r] = B[(bn0 + r) * ldb + bk0 + c];         // n = r, k = c
+  }
+  __syncthreads();
+  const int tx = tid & 15, ty = tid >> 4;
+  double acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+  for (int q = 0; q < NB; ++q) {
+    double av[4], bv[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) av[a] = as[q][ty + 16 * a];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) bv[b] = bs[q][tx + 16 * b];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[a][b] = fma(av[a], bv[b], acc[a][b]);
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      double* c = C + (cm0 + ty + 16 * a) * ldc + cn0 + tx + 16 * b;
+      *c -= acc[a][b];
+    }
+}
+
+// Cholesky trailing update after block column k: lower tiles (ti >= tj) of the
+// trailing matrix, A[i][j] -= L[i][k-block] L[j][k-block]^T.
+__global__ __launch_bounds__(kThreads) void chol_trailing(double* __restrict__ A, int64_t lda, int64_t k) {
+  int64_t ti, tj;
+  tri_tile(blockIdx.x, ti, tj);
+  const int64_t base = (k + 1) * NB;
+  const int64_t i0 = base + ti * NB, j0 = base + tj * NB, k0 = k * NB;
+  tile_update<false>(A, lda, i0, j0, A, lda, i0, k0, A, lda, k0, j0);
+}
+
+// Inverse step i, part 1: X[i][j-block] = Dinv_i * S[i][j-block] for j <= i, in place.
+__global__ __launch_bounds__(kThreads) void inv_rowscale(double* __restrict__ X, int64_t ldx, int64_t i,
+                                                         const double* __restrict__ Dinv) {
+  __shared__ double s[NB][NB + 1];
+  __shared__ double dv[NB][NB + 1];
+  const int tid = threadIdx.x;
+  const int64_t r0 = i * NB, c0 = static_cast<int64_t>(blockIdx.x) * NB;
+  for (int e = tid; e < NB * NB; e += kThreads) {
+    const int r = e / NB, c = e % NB;
+    s[r][c] = X[(r0 + r) * ldx + c0 + c];
+    dv[r][c] = Dinv[i * NB * NB + e];
+  }
+  __syncthreads();
+  for (int e = tid; e < NB * NB; e += kThreads) {
+    const int r = e / NB, c = e % NB;
+    double acc = 0.0;
+    for (int q = 0; q <= r; ++q) acc += dv[r][q] * s[q][c];
+    X[(r0 + r) * ldx + c0 + c] = acc;
+  }
+}
+
+// Inverse step i, part 2: S[r][j] -= L[r][i] X[i][j] for block rows r > i, j <= i.
+__global__ __launch_bounds__(kThreads) void inv_update(double* __restrict__ X, int64_t ldx,
+                                                       const double* __restrict__ L, int64_t ldl,
+                                                       int64_t i) {
+  const int64_t ncol = i + 1;
+  const int64_t rb = i + 1 + blockIdx.x / ncol;
+  const int64_t jb = blockIdx.x % ncol;
+  tile_update<true>(X, ldx, rb * NB, jb * NB, L, ldl, rb * NB, i * NB, X, ldx, i * NB, jb * NB);
+}
+
+__global__ __launch_bounds__(kThreads) void fill_identity(double* __restrict__ X, int64_t ld) {
+  const int64_t total = ld * ld;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x)
+    X[e] = (e / ld == e % ld) ? 1.0 : 0.0;
+}
+
+// Rt[a][b] = R[b][a] = Linv[d-1-b][d-1-a] (zero above the diagonal), fp32.
+__global__ __launch_bounds__(kThreads) void extract_rt(const double* __restrict__ X, int64_t ldx,
+                                                       int64_t d, float* __restrict__ Rt, int64_t ldr) {
+  const int64_t total = d * d;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t a = e / d, b = e % d;
+    Rt[a * ldr + b] = (b <= a) ? static_cast<float>(X[(d - 1 - b) * ldx + (d - 1 - a)]) : 0.0f;
+  }
+}
+
+inline unsigned grid_for(int64_t n) {
+  int64_t b = ceil_div(n, kThreads * 4);
+  if (b > 65536) b = 65536;
+  if (b < 1) b = 1;
+  return static_cast<unsigned>(b);
+}
+
+}  // namespace
+
+size_t rfactor_ws_bytes(int64_t d) {
+  const int64_t dp = round_up(d < 1 ? 1 : d, NB);
+  const int64_t nblk = dp / NB;
+  size_t b = 0;
+  b += align256(static_cast<size_t>(dp) * dp * sizeof(double));   // A -> L
+  b += align256(static_cast<size_t>(dp) * dp * sizeof(double));   // S -> X = L^{-1}
+  b += align256(static_cast<size_t>(nblk) * NB * NB * sizeof(double));
+  b += align256(static_cast<size_t>(dp) * sizeof(double));
+  return b;
+}
+
+int rfactor(const float* H, int64_t d, const int32_t* perm, float* Rt, int64_t ldr, void* ws,
+            uint32_t* flag, hipStream_t s) {
+  const int64_t dp = round_up(d, NB);
+  const int64_t nblk = dp / NB;
+  Carver cv(ws);
+  double* A = cv.take<double>(static_cast<size_t>(dp) * dp);
+  double* X = cv.take<double>(static_cast<size_t>(dp) * dp);
+  double* Dinv = cv.take<double>(static_cast<size_t>(nblk) * NB * NB);
+  double* diag0 = cv.take<double>(static_cast<size_t>(dp));
+
+  init_reversed<<<grid_for(dp * dp), kThreads, 0, s>>>(H, d, perm, A, dp, diag0, flag);
+  QZ_TRY(check_launch("rfactor.init"));
+  for (int64_t k = 0; k < nblk; ++k) {
+    diag_block<<<1, kThreads, 0, s>>>(A, dp, k, diag0, Dinv, flag);
+    QZ_TRY(check_launch("rfactor.diag"));
+    const int64_t below = nblk - k - 1;
+    if (below > 0) {
+      panel_solve<<<static_cast<unsigned>(below), kThreads, 0, s>>>(A, dp, k, Dinv);
+      QZ_TRY(check_launch("rfactor.panel"));
+      chol_trailing<<<static_cast<unsigned>(below * (below + 1) / 2), kThreads, 0, s>>>(A, dp, k);
+      QZ_TRY(check_launch("rfactor.trailing"));
+    }
+  }
+  fill_identity<<<grid_for(dp * dp), kThreads, 0, s>>>(X, dp);
+  QZ_TRY(check_launch("rfactor.fill"));
+  for (int64_t i = 0; i < nblk; ++i) {
+    inv_rowscale<<<static_cast<unsigned>(i + 1), kThreads, 0, s>>>(X, dp, i, Dinv);
+    QZ_TRY(check_launch("rfactor.rowscale"));
+    const int64_t below = nblk - i - 1;
+    if (below > 0) {
+      inv_update<<<static_cast<unsigned>(below * (i + 1)), kThreads, 0, s>>>(X, dp, A, dp, i);
+      QZ_TRY(check_launch("rfactor.invupdate"));
+    }
+  }
+  extract_rt<<<grid_for(d * d), kThreads, 0, s>>>(X, dp, d, Rt, ldr);
+  return check_launch("rfactor.extract");
+}
+
+}  // namespace qz

@@ -1,0 +1,293 @@
+// Grid fit, round-to-nearest, code packing and small conversion kernels.
+//
+// The quantization grid is per (row, group of g consecutive columns), asymmetric,
+// b bits (ADMM-Q summary, 1. problem formulation: the set Q; GPTQ tutorial, section
+// 3: the grid is an input of Algorithm 1).  The fit reading (range forced to hold 0,
+// fp32 arithmetic, half-to-even rounding) is documented in include/qz.h; these
+// kernels reproduce it bit for bit.  Everything here is HBM-bound streaming work.
+#include "qz_internal.h"
+
+namespace qz {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+inline int blocks_for(int64_t n, int per_block, int cap = 1 << 20) {
+  int64_t b = ceil_div(n, per_block);
+  if (b < 1) b = 1;
+  return static_cast<int>(b > cap ? cap : b);
+}
+
+__device__ __forceinline__ void grid_from_range(float lo, float hi, float maxq, float& s,
+                                                float& z) {
+  if (hi == lo) { lo = -1.0f; hi = 1.0f; }
+  s = (hi - lo) / maxq;
+  z = fminf(fmaxf(__builtin_rintf(-lo / s), 0.0f), maxq);
+}
+
+// One thread per (row, group): for small groups.
+template <int WT>
+__global__ __launch_bounds__(kThreads) void grid_fit_thread(
+    const void* __restrict__ W, int64_t rows, int64_t cols, int group, float maxq,
+    float* __restrict__ scales, uint8_t* __restrict__ zeros, float* __restrict__ lo0,
+    float* __restrict__ hi0, uint32_t* __restrict__ flag) {
+  const int64_t G = cols / group;
+  const int64_t total = rows * G;
+  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = t / G, g = t % G;
+    const int64_t base = r * cols + g * group;
+    float lo = 0.0f, hi = 0.0f;
+    bool bad = false;
+    for (int i = 0; i < group; ++i) {
+      float v = load_w<WT>(W, base + i);
+      bad |= !__builtin_isfinite(v);
+      lo = fminf(lo, v);
+      hi = fmaxf(hi, v);
+    }
+    if (bad && flag) atomicOr(flag, FLAG_NONFINITE);
+    float s, z;
+    grid_from_range(lo, hi, maxq, s, z);
+    scales[t] = s;
+    zeros[t] = static_cast<uint8_t>(z);
+    if (lo0) {
+      float l = lo, h = hi;
+      if (h == l) { l = -1.0f; h = 1.0f; }
+      lo0[t] = l;
+      hi0[t] = h;
+    }
+  }
+}
+
+// One wavefront (64 lanes) per (row, group): for groups of 64+ columns.
+template <int WT>
+__global__ __launch_bounds__(kThreads) void grid_fit_wave(
+    const void* __restrict__ W, int64_t rows, int64_t cols, int group, float maxq,
+    float* __restrict__ scales, uint8_t* __restrict__ zeros, float* __restrict__ lo0,
+    float* __restrict__ hi0, uint32_t* __restrict__ flag) {
+  const int lane = threadIdx.x & 63;
+  const int64_t G = cols / group;
+  const int64_t total = rows * G;
+  const int64_t wpb = blockDim.x / 64;
+  for (int64_t t = blockIdx.x * wpb + threadIdx.x / 64; t < total; t += (int64_t)gridDim.x * wpb) {
+    const int64_t r = t / G, g = t % G;
+    const int64_t base = r * cols + g * group;
+    float lo = 0.0f, hi = 0.0f;
+    bool bad = false;
+    for (int i = lane; i < group; i += 64) {
+      float v = load_w<WT>(W, base + i);
+      bad |= !__builtin_isfinite(v);
+      lo = fminf(lo, v);
+      hi = fmaxf(hi, v);
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+      lo = fminf(lo, __shfl_xor(lo, off));
+      hi = fmaxf(hi, __shfl_xor(hi, off));
+    }
+    if (__any(bad) && lane == 0 && flag) atomicOr(flag, FLAG_NONFINITE);
+    if (lane == 0) {
+      float s, z;
+      grid_from_range(lo, hi, maxq, s, z);
+      scales[t] = s;
+      zeros[t] = static_cast<uint8_t>(z);
+      if (lo0) {
+        float l = lo, h = hi;
+        if (h == l) { l = -1.0f; h = 1.0f; }
+        lo0[t] = l;
+        hi0[t] = h;
+      }
+    }
+  }
+}
+
+template <int WT>
+__global__ __launch_bounds__(kThreads) void rtn_kernel(const void* __restrict__ W, int64_t rows,
+                                                       int64_t cols, int group, float maxq,
+                                                       const float* __restrict__ scales,
+                                                       const uint8_t* __restrict__ zeros,
+                                                       uint8_t* __restrict__ codes) {
+  const int64_t G = cols / group;
+  const int64_t total = rows * cols;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = e / cols, c = e % cols;
+    const int64_t gi = r * G + c / group;
+    float x = load_w<WT>(W, e);
+    codes[e] = static_cast<uint8_t>(quant_code(x, scales[gi], static_cast<float>(zeros[gi]), maxq));
+  }
+}
+
+// One thread per packed 32-bit word.
+__global__ __launch_bounds__(kThreads) void pack_kernel(const uint8_t* __restrict__ codes,
+                                                        int64_t rows, int64_t cols, int bits,
+                                                        int64_t words, uint32_t* __restrict__ out) {
+  const int64_t total = rows * words;
+  const uint32_t mask = (1u << bits) - 1u;
+  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = t / words, w = t % words;
+    const int64_t bit0 = w * 32;
+    int64_t i0 = bit0 / bits;
+    int64_t i1 = (bit0 + 31) / bits;
+    if (i1 > cols - 1) i1 = cols - 1;
+    uint32_t acc = 0;
+    for (int64_t i = i0; i <= i1; ++i) {
+      const uint32_t c = codes[r * cols + i] & mask;
+      const int64_t sh = i * bits - bit0;
+      acc |= sh >= 0 ? (c << sh) : (c >> (-sh));
+    }
+    out[t] = acc;
+  }
+}
+
+// One thread per code.
+__global__ __launch_bounds__(kThreads) void unpack_kernel(const uint32_t* __restrict__ in,
+                                                          int64_t rows, int64_t cols, int bits,
+                                                          int64_t words, uint8_t* __restrict__ codes) {
+  const int64_t total = rows * cols;
+  const uint32_t mask = (1u << bits) - 1u;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = e / cols, i = e % cols;
+    const int64_t p = i * bits;
+    const int64_t w = p >> 5;
+    const int off = static_cast<int>(p & 31);
+    uint32_t v = in[r * words + w] >> off;
+    if (off + bits > 32) v |= in[r * words + w + 1] << (32 - off);
+    codes[e] = static_cast<uint8_t>(v & mask);
+  }
+}
+
+template <int WT>
+__global__ __launch_bounds__(kThreads) void to_f32_kernel(const void* __restrict__ W, int64_t rows,
+                                                          int64_t cols, const int32_t* __restrict__ perm,
+                                                          const float* __restrict__ div,
+                                                          float* __restrict__ out, int64_t ldo,
+                                                          uint32_t* __restrict__ flag) {
+  const int64_t total = rows * cols;
+  bool bad = false;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = e / cols, j = e % cols;
+    const int64_t c = perm ? perm[j] : j;
+    float v = load_w<WT>(W, r * cols + c);
+    if (div) v = v / div[c];
+    bad |= !__builtin_isfinite(v);
+    out[r * ldo + j] = v;
+  }
+  if (flag && __any(bad) && (threadIdx.x & 63) == 0) atomicOr(flag, FLAG_NONFINITE);
+}
+
+__global__ __launch_bounds__(kThreads) void finite_kernel(const float* __restrict__ p, int64_t n,
+                                                          uint32_t* __restrict__ flag) {
+  bool bad = false;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n;
+       e += (int64_t)gridDim.x * blockDim.x)
+    bad |= !__builtin_isfinite(p[e]);
+  if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(flag, FLAG_NONFINITE);
+}
+
+__global__ __launch_bounds__(kThreads) void perm_count_kernel(const int32_t* __restrict__ perm,
+                                                              int64_t d, uint32_t* __restrict__ counts,
+                                                              uint32_t* __restrict__ flag) {
+  for (int64_t j = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; j < d;
+       j += (int64_t)gridDim.x * blockDim.x) {
+    const int32_t v = perm[j];
+    if (v < 0 || v >= d) {
+      atomicOr(flag, FLAG_BADARG);
+    } else if (atomicAdd(&counts[v], 1u) != 0u) {
+      atomicOr(flag, FLAG_BADARG);   // duplicate
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void zero_u32_kernel(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t j = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; j < n;
+       j += (int64_t)gridDim.x * blockDim.x)
+    p[j] = 0u;
+}
+
+}  // namespace
+
+int launch_check_perm(const int32_t* perm, int64_t d, uint32_t* counts, uint32_t* flag,
+                      hipStream_t s) {
+  const int nb = blocks_for(d, kThreads, 4096);
+  zero_u32_kernel<<<nb, kThreads, 0, s>>>(counts, d);
+  QZ_TRY(check_launch("check_perm.zero"));
+  perm_count_kernel<<<nb, kThreads, 0, s>>>(perm, d, counts, flag);
+  return check_launch("check_perm");
+}
+
+int launch_grid_fit(const void* W, int wt, int64_t rows, int64_t cols, int group, int bits,
+                    float* scales, uint8_t* zeros, float* lo0, float* hi0, uint32_t* flag,
+                    hipStream_t s) {
+  const float maxq = static_cast<float>((1 << bits) - 1);
+  const int64_t n = rows * (cols / group);
+  if (n == 0) return QZ_OK;
+  if (group >= 64) {
+    int nb = blocks_for(n, kThreads / 64);
+    if (wt == QZ_BF16)
+      grid_fit_wave<QZ_BF16><<<nb, kThreads, 0, s>>>(W, rows, cols, group, maxq, scales, zeros, lo0, hi0, flag);
+    else
+      grid_fit_wave<QZ_F32><<<nb, kThreads, 0, s>>>(W, rows, cols, group, maxq, scales, zeros, lo0, hi0, flag);
+  } else {
+    int nb = blocks_for(n, kThreads);
+    if (wt == QZ_BF16)
+      grid_fit_thread<QZ_BF16><<<nb, kThreads, 0, s>>>(W, rows, cols, group, maxq, scales, zeros, lo0, hi0, flag);
+    else
+      grid_fit_thread<QZ_F32><<<nb, kThreads, 0, s>>>(W, rows, cols, group, maxq, scales, zeros, lo0, hi0, flag);
+  }
+  return check_launch("grid_fit");
+}
+
+int launch_rtn(const void* W, int wt, int64_t rows, int64_t cols, int group, int bits,
+               const float* scales, const uint8_t* zeros, uint8_t* codes, hipStream_t s) {
+  const float maxq = static_cast<float>((1 << bits) - 1);
+  const int64_t n = rows * cols;
+  if (n == 0) return QZ_OK;
+  int nb = blocks_for(n, kThreads * 4, 65536);
+  if (wt == QZ_BF16)
+    rtn_kernel<QZ_BF16><<<nb, kThreads, 0, s>>>(W, rows, cols, group, maxq, scales, zeros, codes);
+  else
+    rtn_kernel<QZ_F32><<<nb, kThreads, 0, s>>>(W, rows, cols, group, maxq, scales, zeros, codes);
+  return check_launch("rtn");
+}
+
+int launch_pack(const uint8_t* codes, int64_t rows, int64_t cols, int bits, uint32_t* out,
+                hipStream_t s) {
+  const int64_t words = ceil_div(cols * bits, 32);
+  const int64_t n = rows * words;
+  if (n == 0) return QZ_OK;
+  pack_kernel<<<blocks_for(n, kThreads, 65536), kThreads, 0, s>>>(codes, rows, cols, bits, words, out);
+  return check_launch("pack");
+}
+
+int launch_unpack(const uint32_t* in, int64_t rows, int64_t cols, int bits, uint8_t* codes,
+                  hipStream_t s) {
+  const int64_t words = ceil_div(cols * bits, 32);
+  const int64_t n = rows * cols;
+  if (n == 0) return QZ_OK;
+  unpack_kernel<<<blocks_for(n, kThreads, 65536), kThreads, 0, s>>>(in, rows, cols, bits, words, codes);
+  return check_launch("unpack");
+}
+
+int launch_to_f32(const void* W, int wt, int64_t rows, int64_t cols, const int32_t* perm,
+                  const float* div, float* out, int64_t ldo, uint32_t* flag, hipStream_t s) {
+  const int64_t n = rows * cols;
+  if (n == 0) return QZ_OK;
+  int nb = blocks_for(n, kThreads * 4, 65536);
+  if (wt == QZ_BF16)
+    to_f32_kernel<QZ_BF16><<<nb, kThreads, 0, s>>>(W, rows, cols, perm, div, out, ldo, flag);
+  else
+    to_f32_kernel<QZ_F32><<<nb, kThreads, 0, s>>>(W, rows, cols, perm, div, out, ldo, flag);
+  return check_launch("to_f32");
+}
+
+int launch_check_finite_f32(const float* p, int64_t n, uint32_t* flag, hipStream_t s) {
+  if (n == 0) return QZ_OK;
+  finite_kernel<<<blocks_for(n, kThreads * 8, 4096), kThreads, 0, s>>>(p, n, flag);
+  return check_launch("check_finite");
+}
+
+}  // namespace qz
