@@ -65,12 +65,19 @@ def compare(H, W, bits, group, iters, rho0, gamma, refresh, flags=0, rows=None, 
     # the iterate's (relative to the row's magnitude), so tiny groups get an absolute floor
     np.testing.assert_allclose(g["scales"][r], o["scale"], rtol=1e-5,
                                atol=1e-5 * float(np.abs(o["scale"]).max()))
-    assert abs(f_gpu - f_ref) <= TOL_OBJECTIVE * max(f_ref, 1e-30)
+    # relative to the oracle's objective, with a floor at 1e-9 of the layer's energy
+    # (1/2) sum w^T H w for layers that the grid represents almost exactly
+    energy = objective.objective(H64, Wf[r], np.zeros_like(Wf[r]))
+    assert abs(f_gpu - f_ref) <= TOL_OBJECTIVE * f_ref + 1e-9 * energy
     if rows is None and iters:
+        # residuals: relative 1e-3, with a floor at fp32 resolution of the scaled weights
+        # (a residual that has converged to ~0 is rounding noise on both sides)
+        wt_norm = float(np.linalg.norm(Wf[r] * np.sqrt(np.diag(H64))[None, :]))
+        rho = rho0 * gamma ** np.arange(iters)
         np.testing.assert_allclose(g["residuals"][:, 0], o["res"][:, 0], rtol=1e-3,
-                                   atol=1e-6 * o["res"][0, 0])
-        np.testing.assert_allclose(g["residuals"][:, 1], o["res"][:, 1], rtol=1e-3,
-                                   atol=1e-6 * max(o["res"][:, 1].max(), 1e-30))
+                                   atol=1e-5 * wt_norm)
+        assert np.all(np.abs(g["residuals"][:, 1] - o["res"][:, 1])
+                      <= 1e-3 * o["res"][:, 1] + 1e-5 * wt_norm * rho)
     return g, o
 
 

@@ -51,7 +51,7 @@ def test_gptq_full_size_sampled_rows(name):
     H64 = Hf.astype(np.float64)
     f_gpu = objective.row_objective(H64, Wf, grid.dequant(c_g, s_g, z_g, group))
     f_ref = objective.row_objective(H64, Wf, grid.dequant(ref, s_ref, z_ref, group))
-    report("gptq_full", name=name, rows=len(rows), adopted=adopted,
+    report("gptq_full", layer=name, rows=len(rows), adopted=adopted,
            max_rel_f=float(np.max(np.abs(f_gpu - f_ref) / f_ref)))
     np.testing.assert_array_equal(c_g, ref)
     assert np.all(np.abs(f_gpu - f_ref) <= TOL_OBJECTIVE * f_ref)
@@ -92,7 +92,7 @@ def test_admm_full_size_sampled_rows(name):
     s0, z0 = grid.fit_grid_f32(Wf, bits, group)
     cg, _ = gptq.gptq(H64, Wf, s0, z0, bits, group, cfg["B"])
     f_gptq = objective.row_objective(H64, Wf, grid.dequant(cg, s0, z0, group))
-    report("admm_full", name=name, rows=len(rows), adopted=o["adopted"],
+    report("admm_full", layer=name, rows=len(rows), adopted=o["adopted"],
            max_rel_f=float(np.max(np.abs(f_gpu - f_ref) / f_ref)),
            f_admm_over_f_gptq=float(f_ref.sum() / f_gptq.sum()))
     np.testing.assert_array_equal(c_g, o["codes"])
