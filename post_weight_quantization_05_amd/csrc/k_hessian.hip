@@ -25,184 +25,356 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef v4i16 __attribute__((address_space(3)))* lds_v4_ptr;
 
-constexpr int HT = 128;         // output tile edge
-constexpr int HBK = 64;         // tokens per K-step
-constexpr int LDH = HBK + 8;    // LDS row length in bf16 (144 bytes: staggers banks)
-constexpr int kThreads = 256;
+constexpr int HT = 256;          // output tile edge
+constexpr int HBK = 32;          // tokens per pipeline stage
+constexpr int LDR = HT + 32;     // LDS row (one token) in bf16: 576 bytes, rows 16 banks apart
+constexpr int kThreads = 512;    // 8 wavefronts: 4 (rows) x 2 (columns), 64 x 128 each
 
 struct HArgs {
   const uint16_t* X;
   int64_t n, d;
-  int64_t T;        // tiles per edge
-  int64_t T_up;     // upper tiles
-  int64_t chunk;    // tokens per split (multiple of HBK)
-  float* partial;   // [S][T_up][HT][HT]
+  int64_t n_tiles;      // upper tiles in the schedule
+  const int32_t* tiles; // [n_tiles][2] = (I, J), I <= J, in schedule order
+  int64_t S;            // token splits
+  int64_t chunk;        // tokens per split (multiple of HBK)
+  float* partial;       // [S][n_tiles][HT][HT]
 };
 
-__device__ __forceinline__ void upper_tile(int64_t t, int64_t T, int64_t& I, int64_t& J) {
-  // row-by-row enumeration of (I, J), I <= J
-  int64_t i = 0, start = 0;
-  while (start + (T - i) <= t) {
-    start += T - i;
-    ++i;
-  }
-  I = i;
-  J = i + (t - start);
-}
-
+// 16-byte load of 8 channels of one token row (zero outside the matrix).
 __device__ __forceinline__ uint4 load8(const uint16_t* __restrict__ X, int64_t row, int64_t n_end,
                                        int64_t col, int64_t d, bool vec_ok) {
   uint4 v = make_uint4(0u, 0u, 0u, 0u);
   if (row >= n_end || col >= d) return v;
   const uint16_t* p = X + row * d + col;
   if (vec_ok && col + 7 < d) return *reinterpret_cast<const uint4*>(p);
-  uint16_t e[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) e[i] = (col + i < d) ? p[i] : uint16_t(0);
-  v.x = e[0] | (uint32_t(e[1]) << 16);
-  v.y = e[2] | (uint32_t(e[3]) << 16);
-  v.z = e[4] | (uint32_t(e[5]) << 16);
-  v.w = e[6] | (uint32_t(e[7]) << 16);
+  auto el = [&](int i) -> uint32_t { return (col + i < d) ? static_cast<uint32_t>(p[i]) : 0u; };
+  v.x = el(0) | (el(1) << 16);
+  v.y = el(2) | (el(3) << 16);
+  v.z = el(4) | (el(5) << 16);
+  v.w = el(6) | (el(7) << 16);
   return v;
 }
 
-__device__ __forceinline__ uint32_t dw(const uint4& v, int q) {
-  return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
+// MFMA operand for a 32-channel column block [c0, c0+32) of a token-major LDS tile,
+// tokens [kb0, kb0+16): lane l gets channel c0 + l%32 at tokens kb0 + 8*(l/32) + 0..7.
+// ds_read_b64_tr_b16 hands lane i of each 16-lane group element i%4 of the chunks
+// addressed by lanes i/4 + 4e (e = 0..3); so lane s of the group addresses token row
+// k + s/4, channels m + 4*(s%4), and lane i receives channel m + i at tokens k..k+3.
+__device__ __forceinline__ bf16x8 operand_tr(const uint16_t* tile, int c0, int kb0, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int m = c0 + 16 * (g & 1) + 4 * (s & 3);
+  const int k = kb0 + 8 * (g >> 1) + (s >> 2);
+  const uint16_t* p0 = tile + k * LDR + m;
+  const uint16_t* p1 = p0 + 4 * LDR;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4_ptr)(p0));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4_ptr)(p1));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, both);
 }
 
-// In-register transpose of an 8 x 8 block of 16-bit values: in[e] holds row e
-// (8 channels), out[m] holds column m (8 tokens).
-__device__ __forceinline__ void transpose8x8(const uint4 in[8], uint4 out[8]) {
+__global__ __launch_bounds__(kThreads, 1) void gram_bf16_kernel(const HArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][HBK * LDR];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][HBK * LDR];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;   // rows 64*wm, columns 128*wn
+
+  // Split-major schedule, gathered per XCD: the hardware deals workgroups round-robin
+  // to the 8 XCDs, so logical ids are regrouped to give each XCD a contiguous run of
+  // (split, tile) pairs -- concurrently resident tiles then read the same token slab
+  // and share it through that XCD's L2.
+  int64_t pid = blockIdx.x;
+  const int64_t nblk = gridDim.x;
+  if ((nblk & 7) == 0) pid = (pid & 7) * (nblk >> 3) + (pid >> 3);
+  const int64_t split = pid / g.n_tiles, t = pid % g.n_tiles;
+  const int64_t I = g.tiles[2 * t], J = g.tiles[2 * t + 1];
+  const bool diag = (I == J);
+  const int64_t i0 = I * HT, j0 = J * HT;
+  const int64_t k_begin = split * g.chunk;
+  int64_t k_end = k_begin + g.chunk;
+  if (k_end > g.n) k_end = g.n;
+  const bool vec_ok = (g.d % 8) == 0;
+
+  // Copy roles: a stage is HBK tokens x 256 channels per panel = 1024 chunks of 16 B;
+  // threads take 2 chunks of A and 2 of B (diagonal tiles: B is A and is not copied).
+  const uint16_t* __restrict__ X = g.X;
+  const int64_t d = g.d;
+  const int crow0 = tid >> 5, crow1 = (tid + kThreads) >> 5;   // token rows 0..31
+  const int ccol = 8 * (tid & 31);                             // channel 0..248
+  uint4 va0, va1, vb0 = make_uint4(0u, 0u, 0u, 0u), vb1 = make_uint4(0u, 0u, 0u, 0u);
+#define QZ_GLOAD(k0)                                                         \
+  do {                                                                       \
+    va0 = load8(X, (k0) + crow0, k_end, i0 + ccol, d, vec_ok);               \
+    va1 = load8(X, (k0) + crow1, k_end, i0 + ccol, d, vec_ok);               \
+    if (!diag) {                                                             \
+      vb0 = load8(X, (k0) + crow0, k_end, j0 + ccol, d, vec_ok);             \
+      vb1 = load8(X, (k0) + crow1, k_end, j0 + ccol, d, vec_ok);             \
+    }                                                                        \
+  } while (0)
+#define QZ_SSTORE(buf)                                                       \
+  do {                                                                       \
+    *reinterpret_cast<uint4*>(&As[buf][crow0 * LDR + ccol]) = va0;           \
+    *reinterpret_cast<uint4*>(&As[buf][crow1 * LDR + ccol]) = va1;           \
+    if (!diag) {                                                             \
+      *reinterpret_cast<uint4*>(&Bs[buf][crow0 * LDR + ccol]) = vb0;         \
+      *reinterpret_cast<uint4*>(&Bs[buf][crow1 * LDR + ccol]) = vb1;         \
+    }                                                                        \
+  } while (0)
+
+  f32x16 acc[2][4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    uint32_t lo[4], hi[4];
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t x = dw(in[2 * p], q), y = dw(in[2 * p + 1], q);
-      lo[p] = (x & 0xffffu) | (y << 16);
-      hi[p] = (x >> 16) | (y & 0xffff0000u);
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+  const int64_t nk = (k_end > k_begin) ? ceil_div(k_end - k_begin, HBK) : 0;
+  if (nk > 0) {
+    QZ_GLOAD(k_begin);
+    QZ_SSTORE(0);
+  }
+  __syncthreads();
+
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    const int buf = static_cast<int>(kt & 1);
+    if (kt + 1 < nk) QZ_GLOAD(k_begin + (kt + 1) * HBK);
+    const uint16_t* as = As[buf];
+    const uint16_t* bs = diag ? As[buf] : Bs[buf];
+#pragma unroll
+    for (int ks = 0; ks < HBK; ks += 16) {
+      bf16x8 a[2], b[4];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) a[mt] = operand_tr(as, wm * 64 + mt * 32, ks, lane);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) b[nt] = operand_tr(bs, wn * 128 + nt * 32, ks, lane);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt], b[nt], acc[mt][nt], 0, 0, 0);
     }
-    out[2 * q] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-    out[2 * q + 1] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    if (kt + 1 < nk) QZ_SSTORE(buf ^ 1);
+    __syncthreads();
+  }
+#undef QZ_GLOAD
+#undef QZ_SSTORE
+
+  // Partial tile, dense [HT][HT] at (split, tile).  Accumulator layout of a 32x32
+  // block: register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+  float* out = g.partial + (split * g.n_tiles + t) * (static_cast<int64_t>(HT) * HT);
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * 64 + mt * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int c = wn * 128 + nt * 32 + (lane & 31);
+        out[row * HT + c] = acc[mt][nt][r];
+      }
+}
+
+// ---------------------------------------------------------------------------------
+// Main path (d % 8 == 0): the same tile, but X streams from HBM straight into a
+// 4-stage LDS ring with global_load_lds_dwordx4 (lane i of a wavefront lands at
+// base + 16 i), so three stages of 32 tokens are in flight while the matrix cores
+// work on the fourth.  LDS rows are one token of 256 channels (512 B, no padding);
+// the 32-byte chunk c of row r is stored at chunk c ^ (2 (r & 3)), which keeps both
+// the transpose reads (4 rows x 2 chunks per half wave) and the DMA writes free of
+// bank conflicts.  Each stage buffer is its own __shared__ object so the compiler's
+// wait-count tracking can tell the stage being read from the stages in flight.
+constexpr int NSTAGE = 4;
+constexpr int PANEL = HBK * HT;   // bf16 elements per panel per stage
+
+__device__ __forceinline__ int swz(int k, int m) {   // element offset of (token k, channel m)
+  return k * HT + 16 * ((m >> 4) ^ (2 * (k & 3))) + (m & 15);
+}
+
+__device__ __forceinline__ bf16x8 operand_swz(const uint16_t* tile, int c0, int kb0, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int m = c0 + 16 * (g & 1) + 4 * (s & 3);
+  const int k = kb0 + 8 * (g >> 1) + (s >> 2);
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4_ptr)(tile + swz(k, m)));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4_ptr)(tile + swz(k + 4, m)));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, both);
+}
+
+// One stage of one panel: 32 token rows = 16 row pairs; wavefront w copies pairs w, w+8.
+__device__ __forceinline__ void dma_panel(uint16_t* dst, const uint16_t* __restrict__ X,
+                                          int64_t k0, int64_t k_end, int64_t col0, int64_t d,
+                                          int wave, int lane) {
+#pragma unroll
+  for (int rep = 0; rep < 2; ++rep) {
+    const int r0 = 2 * (wave + 8 * rep);
+    const int r = r0 + (lane >> 5);
+    const int q = lane & 31;
+    const int c = (q >> 1) ^ (2 * (r & 3));
+    const int64_t grow = k0 + r;
+    const int64_t gcol = col0 + 16 * c + 8 * (q & 1);
+    uint16_t* base = dst + r0 * HT;
+    if (grow < k_end && gcol < d) {
+      // Issued as inline asm so that the compiler does not treat it as an LDS write it
+      // must wait for before every later LDS read: the stages are synchronised by the
+      // explicit vmcnt waits below.  The instruction has no register result.
+      const uint32_t lds_off = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+          reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint16_t*)base)));
+      const uint16_t* src = X + grow * d + gcol;
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                   :
+                   : "s"(lds_off), "v"(src)
+                   : "memory", "m0");
+    } else {
+      *reinterpret_cast<uint4*>(base + 8 * lane) = make_uint4(0u, 0u, 0u, 0u);
+    }
   }
 }
 
-__global__ __launch_bounds__(kThreads, 2) void gram_bf16_kernel(const HArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][HT * LDH];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][HT * LDH];
+// vmcnt(n) for gfx9 encodings: vmcnt bits [3:0] and [15:14]; expcnt/lgkmcnt left at max.
+#define QZ_WAIT_VM(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | (0x7 << 4) | (0xF << 8))
+
+__global__ __launch_bounds__(kThreads, 1) void gram_bf16_dma_kernel(const HArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t L0[2 * PANEL];
+  __shared__ __attribute__((aligned(16))) uint16_t L1[2 * PANEL];
+  __shared__ __attribute__((aligned(16))) uint16_t L2[2 * PANEL];
+  __shared__ __attribute__((aligned(16))) uint16_t L3[2 * PANEL];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  int64_t I, J;
-  upper_tile(blockIdx.x, g.T, I, J);
+  int64_t pid = blockIdx.x;
+  const int64_t nblk = gridDim.x;
+  if ((nblk & 7) == 0) pid = (pid & 7) * (nblk >> 3) + (pid >> 3);
+  const int64_t split = pid / g.n_tiles, t = pid % g.n_tiles;
+  const int64_t I = g.tiles[2 * t], J = g.tiles[2 * t + 1];
   const bool diag = (I == J);
   const int64_t i0 = I * HT, j0 = J * HT;
-  const int64_t k_begin = blockIdx.y * g.chunk;
+  const int64_t k_begin = split * g.chunk;
   int64_t k_end = k_begin + g.chunk;
   if (k_end > g.n) k_end = g.n;
-  const bool vec_ok = (g.d % 8) == 0;
+  const uint16_t* __restrict__ X = g.X;
+  const int64_t d = g.d;
+  const int64_t nk = (k_end > k_begin) ? ceil_div(k_end - k_begin, HBK) : 0;
+  const int64_t n_full = (k_end > k_begin) ? (k_end - k_begin) / HBK : 0;   // stages with 32 tokens
+  const int L = diag ? 2 : 4;   // DMA instructions per stage per wavefront
 
-  // Loader role: threads 0..127 stage the A panel (channels i0..), 128..255 the B
-  // panel (channels j0..); on diagonal tiles B is A and the second half idles.
-  const bool loadB = tid >= 128;
-  const int sub = tid & 127;
-  const int kg = sub >> 4;   // token group of 8 (0..7)
-  const int mg = sub & 15;   // channel group of 8 (0..15)
-  const int64_t col = (loadB ? j0 : i0) + 8 * mg;
-  const bool active_loader = !(loadB && diag);
-
-  uint4 v[8];
-  auto gload = [&](int64_t k0) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      v[e] = active_loader ? load8(g.X, k0 + 8 * kg + e, k_end, col, g.d, vec_ok)
-                           : make_uint4(0u, 0u, 0u, 0u);
-  };
-  auto sstore = [&](int buf) {
-    if (!active_loader) return;
-    uint4 w[8];
-    transpose8x8(v, w);
-    uint16_t* dst = loadB ? Bs[buf] : As[buf];
-#pragma unroll
-    for (int m = 0; m < 8; ++m)
-      *reinterpret_cast<uint4*>(&dst[(8 * mg + m) * LDH + 8 * kg]) = w[m];
-  };
-
-  f32x16 acc[2][2];
+  f32x16 acc[2][4];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-  const int64_t nk = (k_end > k_begin) ? ceil_div(k_end - k_begin, HBK) : 0;
-  if (nk > 0) {
-    gload(k_begin);
-    sstore(0);
-  }
-  __syncthreads();
+#define QZ_ISSUE(BUF, kk)                                                                  \
+  do {                                                                                     \
+    dma_panel(BUF, X, k_begin + (kk) * HBK, k_end, i0, d, wave, lane);                     \
+    if (!diag) dma_panel(BUF + PANEL, X, k_begin + (kk) * HBK, k_end, j0, d, wave, lane);  \
+  } while (0)
 
-  const int lr = lane & 31, lk = 8 * (lane >> 5);
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    const int buf = static_cast<int>(kt & 1);
-    if (kt + 1 < nk) gload(k_begin + (kt + 1) * HBK);
-    const uint16_t* as = As[buf];
-    const uint16_t* bs = diag ? As[buf] : Bs[buf];
-#pragma unroll
-    for (int ks = 0; ks < HBK; ks += 16) {
-      bf16x8 a[2], b[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        a[t] = *reinterpret_cast<const bf16x8*>(&as[(wm * 64 + t * 32 + lr) * LDH + ks + lk]);
-        b[t] = *reinterpret_cast<const bf16x8*>(&bs[(wn * 64 + t * 32 + lr) * LDH + ks + lk]);
-      }
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt], b[nt], acc[mt][nt], 0, 0, 0);
-    }
-    if (kt + 1 < nk) sstore(buf ^ 1);
-    __syncthreads();
+#define QZ_STEP(kk, CUR, NXT)                                                              \
+  if ((kk) < nk) {                                                                         \
+    /* stage kk must have landed: the later stages kk+1, kk+2 may stay in flight */        \
+    const int64_t ahead = ((kk) + 1 < n_full ? 1 : 0) + ((kk) + 2 < n_full ? 1 : 0);        \
+    if (ahead == 2) {                                                                      \
+      if (L == 4) QZ_WAIT_VM(8); else QZ_WAIT_VM(4);                                       \
+    } else if (ahead == 1) {                                                               \
+      if (L == 4) QZ_WAIT_VM(4); else QZ_WAIT_VM(2);                                       \
+    } else {                                                                               \
+      QZ_WAIT_VM(0);                                                                       \
+    }                                                                                      \
+    __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0): zero-fill stores done */            \
+    __builtin_amdgcn_s_barrier();                                                          \
+    if ((kk) + 3 < nk) QZ_ISSUE(NXT, (kk) + 3);                                            \
+    const uint16_t* as = CUR;                                                              \
+    const uint16_t* bs = diag ? CUR : CUR + PANEL;                                         \
+    _Pragma("unroll") for (int ks = 0; ks < HBK; ks += 16) {                               \
+      bf16x8 a[2], b[4];                                                                   \
+      _Pragma("unroll") for (int mt = 0; mt < 2; ++mt)                                     \
+        a[mt] = operand_swz(as, wm * 64 + mt * 32, ks, lane);                              \
+      _Pragma("unroll") for (int nt = 0; nt < 4; ++nt)                                     \
+        b[nt] = operand_swz(bs, wn * 128 + nt * 32, ks, lane);                             \
+      _Pragma("unroll") for (int mt = 0; mt < 2; ++mt)                                     \
+        _Pragma("unroll") for (int nt = 0; nt < 4; ++nt)                                   \
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt], b[nt], acc[mt][nt],  \
+                                                                0, 0, 0);                  \
+    }                                                                                      \
+    /* every wave is done reading CUR before anyone refills it (three steps later) */      \
+    __builtin_amdgcn_s_waitcnt(0xC07F);                                                    \
   }
 
-  // Partial tile, dense [HT][HT] at (split, tile).  Accumulator layout of a 32x32
-  // block: register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l%32.
-  float* out = g.partial + (static_cast<int64_t>(blockIdx.y) * g.T_up + blockIdx.x) * (HT * HT);
+  if (0 < nk) QZ_ISSUE(L0, 0);
+  if (1 < nk) QZ_ISSUE(L1, 1);
+  if (2 < nk) QZ_ISSUE(L2, 2);
+  for (int64_t kt = 0; kt < nk; kt += NSTAGE) {
+    QZ_STEP(kt + 0, L0, L3)
+    QZ_STEP(kt + 1, L1, L0)
+    QZ_STEP(kt + 2, L2, L1)
+    QZ_STEP(kt + 3, L3, L2)
+  }
+#undef QZ_STEP
+#undef QZ_ISSUE
+
+  float* out = g.partial + (split * g.n_tiles + t) * (static_cast<int64_t>(HT) * HT);
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = wm * 64 + mt * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int c = wn * 64 + nt * 32 + (lane & 31);
+        const int c = wn * 128 + nt * 32 + (lane & 31);
         out[row * HT + c] = acc[mt][nt][r];
       }
 }
 
-// Sum the split partials of every upper tile into H (adding the previous raw sum
-// when accumulating).  One thread per tile element.
-__global__ __launch_bounds__(kThreads) void gram_reduce_kernel(const float* __restrict__ partial,
-                                                               int64_t S, int64_t T, int64_t T_up,
-                                                               int64_t d, int accumulate,
-                                                               float* __restrict__ H) {
-  const int64_t per_tile = HT * HT;
-  const int64_t total = T_up * per_tile;
+// Tile schedule: upper tiles (I <= J) grouped in 8 x 8 super-tiles, so that tiles
+// resident at the same time on an XCD share few row and column panels.
+__global__ void schedule_kernel(int64_t T, int32_t* __restrict__ tiles) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  constexpr int64_t SB = 8;
+  const int64_t nS = ceil_div(T, SB);
+  int64_t k = 0;
+  for (int64_t SI = 0; SI < nS; ++SI)
+    for (int64_t SJ = SI; SJ < nS; ++SJ)
+      for (int64_t i = SI * SB; i < (SI + 1) * SB && i < T; ++i)
+        for (int64_t j = SJ * SB; j < (SJ + 1) * SB && j < T; ++j)
+          if (i <= j) {
+            tiles[2 * k] = static_cast<int32_t>(i);
+            tiles[2 * k + 1] = static_cast<int32_t>(j);
+            ++k;
+          }
+}
+
+constexpr int kSmall = 256;   // threads of the auxiliary kernels below
+
+// Sum the split partials of every upper tile into H (adding the previous raw sum when
+// accumulating), fixed order.  One thread per tile element.
+__global__ __launch_bounds__(kSmall) void gram_reduce_kernel(const float* __restrict__ partial,
+                                                             int64_t S, int64_t n_tiles,
+                                                             const int32_t* __restrict__ tiles,
+                                                             int64_t d, int accumulate,
+                                                             float* __restrict__ H) {
+  const int64_t per_tile = static_cast<int64_t>(HT) * HT;
+  const int64_t total = n_tiles * per_tile;
   for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
        e += (int64_t)gridDim.x * blockDim.x) {
     const int64_t t = e / per_tile, rc = e % per_tile;
-    int64_t I, J;
-    upper_tile(t, T, I, J);
-    const int64_t i = I * HT + rc / HT, j = J * HT + rc % HT;
+    const int64_t i = static_cast<int64_t>(tiles[2 * t]) * HT + rc / HT;
+    const int64_t j = static_cast<int64_t>(tiles[2 * t + 1]) * HT + rc % HT;
     if (i >= d || j >= d) continue;
     float s = 0.f;
-    for (int64_t sp = 0; sp < S; ++sp) s += partial[(sp * T_up + t) * per_tile + rc];
+    for (int64_t sp = 0; sp < S; ++sp) s += partial[(sp * n_tiles + t) * per_tile + rc];
     if (accumulate) s += H[i * d + j];
     H[i * d + j] = s;
   }
@@ -210,16 +382,16 @@ __global__ __launch_bounds__(kThreads) void gram_reduce_kernel(const float* __re
 
 // lambda = damp * mean(diag); H_ii += lambda; diag, sigma.  One workgroup, fp64
 // sums in a fixed order.
-__global__ __launch_bounds__(kThreads) void lambda_kernel(float* __restrict__ H, int64_t d,
-                                                          float damp, float* __restrict__ diag,
-                                                          float* __restrict__ sigma,
-                                                          float* __restrict__ lambda_out) {
-  __shared__ double red[kThreads];
+__global__ __launch_bounds__(kSmall) void lambda_kernel(float* __restrict__ H, int64_t d,
+                                                        float damp, float* __restrict__ diag,
+                                                        float* __restrict__ sigma,
+                                                        float* __restrict__ lambda_out) {
+  __shared__ double red[kSmall];
   double s = 0.0;
   for (int64_t i = threadIdx.x; i < d; i += blockDim.x) s += static_cast<double>(H[i * d + i]);
   red[threadIdx.x] = s;
   __syncthreads();
-  for (int w = kThreads / 2; w > 0; w >>= 1) {
+  for (int w = kSmall / 2; w > 0; w >>= 1) {
     if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
     __syncthreads();
   }
@@ -234,12 +406,11 @@ __global__ __launch_bounds__(kThreads) void lambda_kernel(float* __restrict__ H,
 }
 
 // H[j][i] = H[i][j] for i < j, through 32 x 32 LDS tiles (coalesced both ways).
-__global__ __launch_bounds__(kThreads) void mirror_kernel(float* __restrict__ H, int64_t d) {
+__global__ __launch_bounds__(kSmall) void mirror_kernel(float* __restrict__ H, int64_t d) {
   __shared__ float t[32][33];
   const int64_t bi = blockIdx.y, bj = blockIdx.x;   // destination tile (bi, bj), bi >= bj
   if (bj > bi) return;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // 32 x 8
-  // read source tile (bj, bi) from the upper triangle
   for (int r = ty; r < 32; r += 8) {
     const int64_t i = bj * 32 + r, j = bi * 32 + tx;
     t[r][tx] = (i < d && j < d) ? H[i * d + j] : 0.f;
@@ -251,10 +422,10 @@ __global__ __launch_bounds__(kThreads) void mirror_kernel(float* __restrict__ H,
   }
 }
 
-__global__ __launch_bounds__(kThreads) void transpose_f32_kernel(const float* __restrict__ in,
-                                                                 int64_t rows, int64_t cols,
-                                                                 int64_t ldi, float* __restrict__ out,
-                                                                 int64_t ldo) {
+__global__ __launch_bounds__(kSmall) void transpose_f32_kernel(const float* __restrict__ in,
+                                                               int64_t rows, int64_t cols,
+                                                               int64_t ldi, float* __restrict__ out,
+                                                               int64_t ldo) {
   __shared__ float t[32][33];
   const int64_t r0 = blockIdx.y * 32, c0 = blockIdx.x * 32;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
@@ -269,14 +440,40 @@ __global__ __launch_bounds__(kThreads) void transpose_f32_kernel(const float* __
   }
 }
 
-int64_t splits_for(int64_t n, int64_t T_up) {
-  const int64_t target = 1024;   // ~2 resident workgroups on each of 256 CUs, twice
-  int64_t S = ceil_div(target, T_up);
-  const int64_t max_by_n = ceil_div(n, 4 * HBK);
-  if (S > max_by_n) S = max_by_n;
-  if (S > 64) S = 64;
-  if (S < 1) S = 1;
-  return S;
+constexpr int64_t kSlots = 256;   // resident workgroups: one per CU
+
+// Token splits: the smallest S whose rounds of kSlots workgroups waste at most 2% more
+// than the best S <= 32 (each workgroup's work shrinks as 1/S).
+int64_t splits_for(int64_t n, int64_t n_tiles) {
+  int64_t smax = n / (8 * HBK);
+  if (smax > 32) smax = 32;
+  if (smax < 1) smax = 1;
+  double best = 1e300;
+  for (int64_t S = 1; S <= smax; ++S) {
+    const double cost = static_cast<double>(ceil_div(n_tiles * S, kSlots)) / S;
+    if (cost < best) best = cost;
+  }
+  for (int64_t S = 1; S <= smax; ++S) {
+    const double cost = static_cast<double>(ceil_div(n_tiles * S, kSlots)) / S;
+    if (cost <= best * 1.02) return S;
+  }
+  return 1;
+}
+
+struct HPlan {
+  int64_t T, n_tiles, S, chunk;
+  size_t tiles_bytes, partial_bytes;
+};
+
+HPlan plan_for(int64_t n, int64_t d) {
+  HPlan p;
+  p.T = ceil_div(d, HT);
+  p.n_tiles = p.T * (p.T + 1) / 2;
+  p.S = splits_for(n, p.n_tiles);
+  p.chunk = round_up(ceil_div(n > 0 ? n : 1, p.S), HBK);
+  p.tiles_bytes = align256(static_cast<size_t>(p.n_tiles) * 2 * sizeof(int32_t));
+  p.partial_bytes = align256(static_cast<size_t>(p.S) * p.n_tiles * HT * HT * sizeof(float));
+  return p;
 }
 
 }  // namespace
@@ -285,16 +482,14 @@ int launch_transpose_f32(const float* in, int64_t rows, int64_t cols, int64_t ld
                          int64_t ldo, hipStream_t s) {
   if (rows == 0 || cols == 0) return QZ_OK;
   dim3 grid(static_cast<unsigned>(ceil_div(cols, 32)), static_cast<unsigned>(ceil_div(rows, 32)));
-  transpose_f32_kernel<<<grid, kThreads, 0, s>>>(in, rows, cols, ldi, out, ldo);
+  transpose_f32_kernel<<<grid, kSmall, 0, s>>>(in, rows, cols, ldi, out, ldo);
   return check_launch("transpose_f32");
 }
 
 size_t hessian_ws_bytes(int64_t n, int64_t d, int xt) {
   if (xt == QZ_F32) return align256(static_cast<size_t>(round_up(d, 4)) * round_up(n, 4) * 4);
-  const int64_t T = ceil_div(d, HT);
-  const int64_t T_up = T * (T + 1) / 2;
-  const int64_t S = splits_for(n, T_up);
-  return align256(static_cast<size_t>(S) * T_up * HT * HT * sizeof(float));
+  const HPlan p = plan_for(n, d);
+  return p.tiles_bytes + p.partial_bytes;
 }
 
 int hessian_build(const void* X, int xt, int64_t n, int64_t d, float damp, uint32_t flags,
@@ -302,26 +497,32 @@ int hessian_build(const void* X, int xt, int64_t n, int64_t d, float damp, uint3
                   size_t ws_bytes, hipStream_t s) {
   const bool accumulate = flags & QZ_H_ACCUMULATE;
   if (xt == QZ_BF16) {
+    const HPlan p = plan_for(n, d);
+    if (p.n_tiles * p.S > 0x7fffffff) return fail(QZ_EINVAL, "hessian: d too large");
     HArgs g;
     g.X = static_cast<const uint16_t*>(X);
     g.n = n;
     g.d = d;
-    g.T = ceil_div(d, HT);
-    g.T_up = g.T * (g.T + 1) / 2;
-    const int64_t S = splits_for(n, g.T_up);
-    g.chunk = round_up(ceil_div(n, S), HBK);
-    g.partial = static_cast<float*>(ws);
-    if (g.T_up > 0x7fffffff) return fail(QZ_EINVAL, "hessian: d too large");
-    dim3 grid(static_cast<unsigned>(g.T_up), static_cast<unsigned>(S));
+    g.n_tiles = p.n_tiles;
+    g.tiles = reinterpret_cast<int32_t*>(ws);
+    g.S = p.S;
+    g.chunk = p.chunk;
+    g.partial = reinterpret_cast<float*>(static_cast<char*>(ws) + p.tiles_bytes);
+    schedule_kernel<<<1, 64, 0, s>>>(p.T, const_cast<int32_t*>(g.tiles));
+    QZ_TRY(check_launch("gram_schedule"));
     {
       ScopedTimer tm(K_HESSIAN_GRAM, s);
-      gram_bf16_kernel<<<grid, kThreads, 0, s>>>(g);
+      if (d % 8 == 0)
+        gram_bf16_dma_kernel<<<static_cast<unsigned>(p.n_tiles * p.S), kThreads, 0, s>>>(g);
+      else
+        gram_bf16_kernel<<<static_cast<unsigned>(p.n_tiles * p.S), kThreads, 0, s>>>(g);
       QZ_TRY(check_launch("gram_bf16"));
     }
     ScopedTimer tm(K_HESSIAN_FINISH, s);
-    const int64_t total = g.T_up * HT * HT;
-    int nb = static_cast<int>(ceil_div(total, kThreads) > 65536 ? 65536 : ceil_div(total, kThreads));
-    gram_reduce_kernel<<<nb, kThreads, 0, s>>>(g.partial, S, g.T, g.T_up, d, accumulate ? 1 : 0, H);
+    const int64_t total = p.n_tiles * HT * HT;
+    const int nb = static_cast<int>(ceil_div(total, kSmall) > 65536 ? 65536 : ceil_div(total, kSmall));
+    gram_reduce_kernel<<<nb, kSmall, 0, s>>>(g.partial, p.S, p.n_tiles, g.tiles, d,
+                                             accumulate ? 1 : 0, H);
     QZ_TRY(check_launch("gram_reduce"));
   } else {
     // fp32 input: X^T staged K-contiguous, then the fp32 matrix-core GEMM.
@@ -338,11 +539,11 @@ int hessian_build(const void* X, int xt, int64_t n, int64_t d, float damp, uint3
   }
   if (!(flags & QZ_H_NO_FINALIZE)) {
     ScopedTimer tm(K_HESSIAN_FINISH, s);
-    lambda_kernel<<<1, kThreads, 0, s>>>(H, d, damp, diag, sigma, lambda_out);
+    lambda_kernel<<<1, kSmall, 0, s>>>(H, d, damp, diag, sigma, lambda_out);
     QZ_TRY(check_launch("lambda"));
     const int64_t nt = ceil_div(d, 32);
     dim3 grid(static_cast<unsigned>(nt), static_cast<unsigned>(nt));
-    mirror_kernel<<<grid, kThreads, 0, s>>>(H, d);
+    mirror_kernel<<<grid, kSmall, 0, s>>>(H, d);
     QZ_TRY(check_launch("mirror"));
   }
   (void)ws_bytes;
