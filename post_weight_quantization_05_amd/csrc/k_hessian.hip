@@ -183,13 +183,12 @@ __global__ __launch_bounds__(kThreads, 1) void gram_bf16_kernel(const HArgs g) {
 
 // ---------------------------------------------------------------------------------
 // Main path (d % 8 == 0): the same tile, but X streams from HBM straight into a
-// 4-stage LDS ring with global_load_lds_dwordx4 (lane i of a wavefront lands at
-// base + 16 i), so three stages of 32 tokens are in flight while the matrix cores
-// work on the fourth.  LDS rows are one token of 256 channels (512 B, no padding);
+// ring of four 32-token stage buffers with global_load_lds_dwordx4 (lane i of a
+// wavefront lands at base + 16 i), so the next 64 tokens stream in while the matrix
+// cores work on the current 64.  LDS rows are one token of 256 channels (512 B, no padding);
 // the 32-byte chunk c of row r is stored at chunk c ^ (2 (r & 3)), which keeps both
 // the transpose reads (4 rows x 2 chunks per half wave) and the DMA writes free of
-// bank conflicts.  Each stage buffer is its own __shared__ object so the compiler's
-// wait-count tracking can tell the stage being read from the stages in flight.
+// bank conflicts.
 constexpr int NSTAGE = 4;
 constexpr int PANEL = HBK * HT;   // bf16 elements per panel per stage
 
@@ -238,9 +237,11 @@ __device__ __forceinline__ void dma_panel(uint16_t* dst, const uint16_t* __restr
   }
 }
 
-// vmcnt(n) for gfx9 encodings: vmcnt bits [3:0] and [15:14]; expcnt/lgkmcnt left at max.
-#define QZ_WAIT_VM(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | (0x7 << 4) | (0xF << 8))
-
+// Pipeline: four stage buffers used as two pairs.  After one barrier the wavefronts
+// issue the DMA of the next pair of stages (into the pair consumed before the barrier)
+// and then run the matrix cores over the current pair (64 tokens: 32 MFMAs per
+// wavefront); the next barrier first waits for that DMA.  One barrier per 64 tokens
+// keeps the two wavefronts of a SIMD from stalling in lock-step on every 32 tokens.
 __global__ __launch_bounds__(kThreads, 1) void gram_bf16_dma_kernel(const HArgs g) {
   __shared__ __attribute__((aligned(16))) uint16_t L0[2 * PANEL];
   __shared__ __attribute__((aligned(16))) uint16_t L1[2 * PANEL];
@@ -265,8 +266,6 @@ __global__ __launch_bounds__(kThreads, 1) void gram_bf16_dma_kernel(const HArgs 
   const uint16_t* __restrict__ X = g.X;
   const int64_t d = g.d;
   const int64_t nk = (k_end > k_begin) ? ceil_div(k_end - k_begin, HBK) : 0;
-  const int64_t n_full = (k_end > k_begin) ? (k_end - k_begin) / HBK : 0;   // stages with 32 tokens
-  const int L = diag ? 2 : 4;   // DMA instructions per stage per wavefront
 
   f32x16 acc[2][4];
 #pragma unroll
@@ -282,20 +281,8 @@ __global__ __launch_bounds__(kThreads, 1) void gram_bf16_dma_kernel(const HArgs 
     if (!diag) dma_panel(BUF + PANEL, X, k_begin + (kk) * HBK, k_end, j0, d, wave, lane);  \
   } while (0)
 
-#define QZ_STEP(kk, CUR, NXT)                                                              \
-  if ((kk) < nk) {                                                                         \
-    /* stage kk must have landed: the later stages kk+1, kk+2 may stay in flight */        \
-    const int64_t ahead = ((kk) + 1 < n_full ? 1 : 0) + ((kk) + 2 < n_full ? 1 : 0);        \
-    if (ahead == 2) {                                                                      \
-      if (L == 4) QZ_WAIT_VM(8); else QZ_WAIT_VM(4);                                       \
-    } else if (ahead == 1) {                                                               \
-      if (L == 4) QZ_WAIT_VM(4); else QZ_WAIT_VM(2);                                       \
-    } else {                                                                               \
-      QZ_WAIT_VM(0);                                                                       \
-    }                                                                                      \
-    __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0): zero-fill stores done */            \
-    __builtin_amdgcn_s_barrier();                                                          \
-    if ((kk) + 3 < nk) QZ_ISSUE(NXT, (kk) + 3);                                            \
+#define QZ_COMPUTE(CUR)                                                                    \
+  {                                                                                        \
     const uint16_t* as = CUR;                                                              \
     const uint16_t* bs = diag ? CUR : CUR + PANEL;                                         \
     _Pragma("unroll") for (int ks = 0; ks < HBK; ks += 16) {                               \
@@ -309,20 +296,28 @@ __global__ __launch_bounds__(kThreads, 1) void gram_bf16_dma_kernel(const HArgs 
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt], b[nt], acc[mt][nt],  \
                                                                 0, 0, 0);                  \
     }                                                                                      \
-    /* every wave is done reading CUR before anyone refills it (three steps later) */      \
-    __builtin_amdgcn_s_waitcnt(0xC07F);                                                    \
+  }
+
+// vmcnt(0) (the pair's DMA landed) and lgkmcnt(0) (zero fills and this wave's LDS reads
+// done), then the workgroup barrier.  s_waitcnt 0x0070: vmcnt 0, expcnt 7, lgkmcnt 0.
+#define QZ_PAIR(kk, C0, C1, N0, N1)                                                        \
+  if ((kk) < nk) {                                                                         \
+    __builtin_amdgcn_s_waitcnt(0x0070);                                                    \
+    __builtin_amdgcn_s_barrier();                                                          \
+    if ((kk) + 2 < nk) QZ_ISSUE(N0, (kk) + 2);                                             \
+    if ((kk) + 3 < nk) QZ_ISSUE(N1, (kk) + 3);                                             \
+    QZ_COMPUTE(C0)                                                                         \
+    if ((kk) + 1 < nk) QZ_COMPUTE(C1)                                                      \
   }
 
   if (0 < nk) QZ_ISSUE(L0, 0);
   if (1 < nk) QZ_ISSUE(L1, 1);
-  if (2 < nk) QZ_ISSUE(L2, 2);
   for (int64_t kt = 0; kt < nk; kt += NSTAGE) {
-    QZ_STEP(kt + 0, L0, L3)
-    QZ_STEP(kt + 1, L1, L0)
-    QZ_STEP(kt + 2, L2, L1)
-    QZ_STEP(kt + 3, L3, L2)
+    QZ_PAIR(kt + 0, L0, L1, L2, L3)
+    QZ_PAIR(kt + 2, L2, L3, L0, L1)
   }
-#undef QZ_STEP
+#undef QZ_PAIR
+#undef QZ_COMPUTE
 #undef QZ_ISSUE
 
   float* out = g.partial + (split * g.n_tiles + t) * (static_cast<int64_t>(HT) * HT);
