@@ -27,7 +27,7 @@ namespace qz {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kProjBlocks = 2048;
+constexpr int kProjBlocks = 16384;   // many resident waves: more bytes in flight
 
 __global__ __launch_bounds__(kThreads) void project_kernel(const AdmmProj p,
                                                            const float* __restrict__ inv_sigma) {
@@ -96,6 +96,151 @@ __global__ __launch_bounds__(kThreads) void project_kernel(const AdmmProj p,
     }
   }
   // wavefront then workgroup reduction (fixed order)
+  for (int off = 32; off > 0; off >>= 1) {
+    acc_p += __shfl_xor(acc_p, off);
+    acc_d += __shfl_xor(acc_d, off);
+  }
+  if (lane == 0) {
+    red[wid][0] = acc_p;
+    red[wid][1] = acc_d;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double sp = 0.0, sd = 0.0;
+    for (int w = 0; w < kThreads / 64; ++w) {
+      sp += red[w][0];
+      sd += red[w][1];
+    }
+    const double rho = p.rho;
+    p.partial[2 * blockIdx.x] = sp;
+    p.partial[2 * blockIdx.x + 1] = rho * rho * sd;
+  }
+}
+
+// Register-resident variant for groups of exactly 64*EPL columns (64, 128, 256): lane l
+// owns EPL consecutive columns of the group and loads them once with vector loads (the
+// min/max of the refresh comes from the registers, no second pass over memory).
+template <int EPL>
+struct Vec;
+template <>
+struct Vec<1> { typedef float T; typedef uint8_t C; };
+template <>
+struct Vec<2> { typedef float2 T; typedef ushort C; };
+template <>
+struct Vec<4> { typedef float4 T; typedef uint32_t C; };
+
+template <int EPL>
+__device__ __forceinline__ void vload(const float* p, float (&v)[EPL]) {
+  typedef typename Vec<EPL>::T T;
+  const T x = *reinterpret_cast<const T*>(p);
+  __builtin_memcpy(v, &x, sizeof(T));
+}
+template <int EPL>
+__device__ __forceinline__ void vstore(float* p, const float (&v)[EPL]) {
+  typedef typename Vec<EPL>::T T;
+  T x;
+  __builtin_memcpy(&x, v, sizeof(T));
+  *reinterpret_cast<T*>(p) = x;
+}
+template <int EPL>
+__device__ __forceinline__ void cload(const uint8_t* p, uint8_t (&c)[EPL]) {
+  typedef typename Vec<EPL>::C C;
+  const C x = *reinterpret_cast<const C*>(p);
+  __builtin_memcpy(c, &x, sizeof(C));
+}
+template <int EPL>
+__device__ __forceinline__ void cstore(uint8_t* p, const uint8_t (&c)[EPL]) {
+  typedef typename Vec<EPL>::C C;
+  C x;
+  __builtin_memcpy(&x, c, sizeof(C));
+  *reinterpret_cast<C*>(p) = x;
+}
+
+template <int EPL>
+__global__ __launch_bounds__(kThreads) void project_reg_kernel(const AdmmProj p,
+                                                               const float* __restrict__ inv_sigma) {
+  constexpr int UNR = 1;
+  __shared__ double red[kThreads / 64][2];
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int64_t G = p.d_i / p.group;
+  const int64_t total = p.d_o * G;
+  const float maxq = static_cast<float>((1 << p.bits) - 1);
+  const int64_t wstride = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
+  const float rs = p.rescale ? p.rho / p.rho_next : 1.0f;
+  double acc_p = 0.0, acc_d = 0.0;
+
+  for (int64_t t0 = (blockIdx.x * (kThreads / 64) + wid) * UNR; t0 < total; t0 += wstride * UNR) {
+    float w[UNR][EPL], u[UNR][EPL], sg[UNR][EPL], isg[UNR][EPL];
+    uint8_t cd[UNR][EPL];
+    int64_t rr[UNR], cc[UNR];
+    bool live[UNR];
+#pragma unroll
+    for (int k = 0; k < UNR; ++k) {
+      const int64_t t = t0 + k;
+      live[k] = t < total;
+      const int64_t tt = live[k] ? t : t0;
+      rr[k] = tt / G;
+      cc[k] = (tt % G) * p.group + lane * EPL;
+      vload<EPL>(p.Wt + rr[k] * p.ldw + cc[k], w[k]);
+      vload<EPL>(p.U + rr[k] * p.d_i + cc[k], u[k]);
+      vload<EPL>(p.sigma + cc[k], sg[k]);
+      vload<EPL>(inv_sigma + cc[k], isg[k]);
+      cload<EPL>(p.codes + rr[k] * p.d_i + cc[k], cd[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < UNR; ++k) {
+      if (!live[k]) continue;   // wave-uniform
+      const int64_t t = t0 + k;
+      const float s_old = p.scales[t];
+      const float z_old = static_cast<float>(p.zeros[t]);
+      float s = s_old, z = z_old;
+      if (p.refresh) {
+        float lo = 0.f, hi = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          float v = w[k][e];
+          if (p.refresh == 3) v += u[k][e];
+          v *= sg[k][e];
+          lo = fminf(lo, v);
+          hi = fmaxf(hi, v);
+        }
+        for (int off = 32; off > 0; off >>= 1) {
+          lo = fminf(lo, __shfl_xor(lo, off));
+          hi = fmaxf(hi, __shfl_xor(hi, off));
+        }
+        if (hi == lo) { lo = -1.f; hi = 1.f; }
+        if (p.refresh != 2) {
+          lo = fmaxf(lo, p.lo0[t]);
+          hi = fminf(hi, p.hi0[t]);
+        }
+        s = (hi - lo) / maxq;
+        z = fminf(fmaxf(__builtin_rintf(-lo / s), 0.f), maxq);
+      }
+      float un[EPL], mm[EPL];
+      uint8_t cn[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const float zv = (w[k][e] + u[k][e]) * sg[k][e];
+        const float c = quant_code(zv, s, z, maxq);
+        const float dt = s * (c - z) * isg[k][e];
+        const float dold = s_old * (static_cast<float>(cd[k][e]) - z_old) * isg[k][e];
+        un[e] = (u[k][e] + w[k][e] - dt) * rs;
+        mm[e] = dt - un[e];
+        cn[e] = static_cast<uint8_t>(c);
+        const float ep = w[k][e] - dt, ed = dt - dold;
+        acc_p += static_cast<double>(ep) * ep;
+        acc_d += static_cast<double>(ed) * ed;
+      }
+      vstore<EPL>(p.U + rr[k] * p.d_i + cc[k], un);
+      vstore<EPL>(p.M + rr[k] * p.ldm + cc[k], mm);
+      cstore<EPL>(p.codes + rr[k] * p.d_i + cc[k], cn);
+      if (p.refresh && lane == 0) {
+        p.scales[t] = s;
+        p.zeros[t] = static_cast<uint8_t>(z);
+      }
+    }
+  }
   for (int off = 32; off > 0; off >>= 1) {
     acc_p += __shfl_xor(acc_p, off);
     acc_d += __shfl_xor(acc_d, off);
@@ -210,7 +355,17 @@ inline unsigned grid_for(int64_t n) {
 int admm_proj_blocks() { return kProjBlocks; }
 
 int launch_admm_project(const AdmmProj& p, hipStream_t s, const float* inv_sigma) {
-  project_kernel<<<kProjBlocks, kThreads, 0, s>>>(p, inv_sigma);
+  // register-resident path when a group is exactly 64, 128 or 256 columns and every row
+  // start is aligned for the vector loads
+  const bool al = (p.d_i % 4 == 0) && (p.ldw % 4 == 0) && (p.ldm % 4 == 0);
+  if (al && p.group == 128)
+    project_reg_kernel<2><<<kProjBlocks, kThreads, 0, s>>>(p, inv_sigma);
+  else if (al && p.group == 256)
+    project_reg_kernel<4><<<kProjBlocks, kThreads, 0, s>>>(p, inv_sigma);
+  else if (p.group == 64)
+    project_reg_kernel<1><<<kProjBlocks, kThreads, 0, s>>>(p, inv_sigma);
+  else
+    project_kernel<<<kProjBlocks, kThreads, 0, s>>>(p, inv_sigma);
   return check_launch("admm_project");
 }
 
