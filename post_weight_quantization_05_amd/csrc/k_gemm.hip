@@ -8,12 +8,17 @@
 //    the batched update that turns the column loop into matrix products).
 //
 // Both operands are read K-contiguous ("NT" form), which is how every caller stores
-// them, so tiles stage straight into LDS without a transpose.  Tiles of 128 x 128
-// per 256-thread workgroup, 4 wavefronts each owning 64 x 64 = 2 x 2 blocks of
-// v_mfma_f32_32x32x2_f32; K advances 32 at a time with double-buffered LDS and
-// register prefetch of the next slab.  The K index within an 8-wide slab is split
-// as k = 4 * (lane / 32) + e between the two lane halves, identically for A and B,
-// so each lane reads one 16-byte vector per operand and feeds four MFMAs.
+// them, so tiles stage straight into LDS without a transpose.  Tiles of 128 x 128 per
+// 256-thread workgroup, 4 wavefronts each owning 64 x 64 = 2 x 2 blocks of
+// v_mfma_f32_32x32x2_f32.  K advances 64 at a time: the next 64-deep slab of both
+// operands is prefetched into registers (16 x 16 B per thread) while the matrix cores
+// work through the current slab in LDS (128 MFMAs of 64 cycles per wavefront between
+// barriers), then written to the single, row-padded LDS buffer.  Two workgroups fit
+// per CU (70 KB of LDS each), so one workgroup's barrier phase is covered by the
+// other's MFMAs.  The K index within an 8-wide group is split k = 4 * (lane / 32) + e
+// between the two lane halves, identically for A and B, so each lane reads one 16-byte
+// vector per operand and feeds four MFMAs.  Interior tiles (whole tile and every slab
+// inside the matrices) use unchecked vector loads; edge tiles check every element.
 #include "qz_internal.h"
 
 namespace qz {
@@ -22,17 +27,18 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128, BN = 128, BK = 32;
-constexpr int LDK = BK + 4;  // padded LDS row (floats): shifts rows across banks
+constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int LDK = BK + 4;  // padded LDS row (floats): rows 4 banks apart
 constexpr int kThreads = 256;
+constexpr int PER = (BM * BK / 4) / kThreads;   // float4 chunks per operand per thread (8)
 
-template <bool VEC>
-__device__ __forceinline__ float4 load4(const float* __restrict__ base, int64_t row, int64_t nrows,
-                                        int64_t ld, int64_t k, int64_t K) {
+__device__ __forceinline__ float4 load4_checked(const float* __restrict__ base, int64_t row,
+                                                int64_t nrows, int64_t ld, int64_t k, int64_t K,
+                                                bool vec) {
   float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
   if (row >= nrows) return v;
   const float* p = base + row * ld + k;
-  if (VEC && k + 3 < K) return *reinterpret_cast<const float4*>(p);
+  if (vec && k + 3 < K) return *reinterpret_cast<const float4*>(p);
   if (k + 0 < K) v.x = p[0];
   if (k + 1 < K) v.y = p[1];
   if (k + 2 < K) v.z = p[2];
@@ -56,8 +62,8 @@ __device__ __forceinline__ void tile_coords(int64_t pid, int64_t tm_n, int64_t t
 
 template <int EPI, bool VEC>
 __global__ __launch_bounds__(kThreads, 2) void gemm_nt_kernel(const GemmArgs g) {
-  __shared__ float As[2][BM * LDK];
-  __shared__ float Bs[2][BN * LDK];
+  __shared__ __attribute__((aligned(16))) float As[BM * LDK];
+  __shared__ __attribute__((aligned(16))) float Bs[BN * LDK];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -73,6 +79,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_nt_kernel(const GemmArgs g) 
   int64_t tm, tn;
   tile_coords(pid, tm_n, tn_n, tm, tn);
   const int64_t m0 = tm * BM, n0 = tn * BN;
+  const bool interior = VEC && (m0 + BM <= g.M) && (n0 + BN <= g.N) && (g.K % BK == 0);
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -82,57 +89,65 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_nt_kernel(const GemmArgs g) 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  float4 ra[4], rb[4];
+  // thread's chunks: chunk f = tid + 256 i -> row f / 16, float4 column f % 16
+  const int crow = tid >> 4, ccol = 4 * (tid & 15);
+  float4 ra[PER], rb[PER];
+  const float* __restrict__ Ab = g.A + (m0 + crow) * g.lda + ccol;
+  const float* __restrict__ Bb = g.B + (n0 + crow) * g.ldb + ccol;
+  const int64_t a_step = 16 * g.lda, b_step = 16 * g.ldb;
+
   auto gload = [&](int64_t k0) {
+    if (interior) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int f = tid + kThreads * i;
-      const int row = f >> 3, c4 = f & 7;
-      ra[i] = load4<VEC>(g.A, m0 + row, g.M, g.lda, k0 + 4 * c4, g.K);
-      rb[i] = load4<VEC>(g.B, n0 + row, g.N, g.ldb, k0 + 4 * c4, g.K);
+      for (int i = 0; i < PER; ++i) {
+        ra[i] = *reinterpret_cast<const float4*>(Ab + i * a_step + k0);
+        rb[i] = *reinterpret_cast<const float4*>(Bb + i * b_step + k0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        ra[i] = load4_checked(g.A, m0 + crow + 16 * i, g.M, g.lda, k0 + ccol, g.K, VEC);
+        rb[i] = load4_checked(g.B, n0 + crow + 16 * i, g.N, g.ldb, k0 + ccol, g.K, VEC);
+      }
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&]() {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int f = tid + kThreads * i;
-      const int row = f >> 3, c4 = f & 7;
-      *reinterpret_cast<float4*>(&As[buf][row * LDK + 4 * c4]) = ra[i];
-      *reinterpret_cast<float4*>(&Bs[buf][row * LDK + 4 * c4]) = rb[i];
+    for (int i = 0; i < PER; ++i) {
+      *reinterpret_cast<float4*>(&As[(crow + 16 * i) * LDK + ccol]) = ra[i];
+      *reinterpret_cast<float4*>(&Bs[(crow + 16 * i) * LDK + ccol]) = rb[i];
     }
   };
 
   const int64_t nk = ceil_div(g.K, BK);
   gload(0);
-  sstore(0);
+  sstore();
   __syncthreads();
 
   const int lr = lane & 31, lk = 4 * (lane >> 5);
   for (int64_t kt = 0; kt < nk; ++kt) {
-    const int buf = static_cast<int>(kt & 1);
     if (kt + 1 < nk) gload((kt + 1) * BK);
-    const float* as = As[buf];
-    const float* bs = Bs[buf];
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 8) {
       float4 a[2], b[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        a[t] = *reinterpret_cast<const float4*>(&as[(wm * 64 + t * 32 + lr) * LDK + kk + lk]);
-        b[t] = *reinterpret_cast<const float4*>(&bs[(wn * 64 + t * 32 + lr) * LDK + kk + lk]);
+        a[t] = *reinterpret_cast<const float4*>(&As[(wm * 64 + t * 32 + lr) * LDK + kk + lk]);
+        b[t] = *reinterpret_cast<const float4*>(&Bs[(wn * 64 + t * 32 + lr) * LDK + kk + lk]);
       }
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int e = 0; e < 4; ++e)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[mt].x, b[nt].x, acc[mt][nt], 0, 0, 0);
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[mt].y, b[nt].y, acc[mt][nt], 0, 0, 0);
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[mt].z, b[nt].z, acc[mt][nt], 0, 0, 0);
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[mt].w, b[nt].w, acc[mt][nt], 0, 0, 0);
-        }
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[mt][e], b[nt][e], acc[mt][nt], 0, 0, 0);
     }
-    if (kt + 1 < nk) sstore(buf ^ 1);
-    __syncthreads();
+    if (kt + 1 < nk) {
+      __syncthreads();   // every wave is done with the slab in LDS
+      sstore();
+      __syncthreads();
+    }
   }
 
   // Epilogue.  32x32 accumulator layout: register r of lane l holds
