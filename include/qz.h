@@ -21,7 +21,10 @@
  * - All array arguments are DEVICE pointers unless the comment says "host".
  *   The caller owns every buffer; the library never frees caller memory.
  *   Work buffers come from the caller through `ws`/`ws_bytes`, sized by the
- *   matching *_workspace() query; a smaller buffer gives QZ_EWORKSPACE.
+ *   matching *_workspace() query and 256-byte aligned (as hipMalloc returns
+ *   them); a smaller or misaligned buffer gives QZ_EWORKSPACE.  Other arrays
+ *   need only their element type's alignment (vector paths check and fall
+ *   back to element access).
  *   (qz_admmq_prepare is the exception: the eigen-solver library it calls
  *   manages its own device memory.)
  * - Matrices are dense row-major with the leading dimension equal to the

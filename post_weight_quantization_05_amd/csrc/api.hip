@@ -115,6 +115,8 @@ int qz_build_hessian(const void* X, int32_t xt, int64_t n, int64_t d_i, float da
   if (flags & ~(QZ_H_ACCUMULATE | QZ_H_NO_FINALIZE)) return fail(QZ_EINVAL, "build_hessian: unknown flags");
   const size_t need = hessian_ws_bytes(n, d_i, xt);
   if (ws_bytes < need || (need > 0 && !ws)) return fail(QZ_EWORKSPACE, "build_hessian: workspace too small");
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0)
+    return fail(QZ_EWORKSPACE, "build_hessian: workspace must be 256-byte aligned");
   set_error("");
   return hessian_build(X, xt, n, d_i, damp, flags, H, diag, sigma, lambda_out, ws, ws_bytes, stream);
 }
@@ -161,6 +163,8 @@ int qz_gptq(const float* H, const void* W_hat, int32_t wt, int64_t d_o, int64_t 
     return fail(QZ_EINVAL, "gptq: null pointer");
   const size_t need = gptq_ws(d_o, d_i);
   if (ws_bytes < need || !ws) return fail(QZ_EWORKSPACE, "gptq: workspace too small");
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0)
+    return fail(QZ_EWORKSPACE, "gptq: workspace must be 256-byte aligned");
   set_error("");
 
   const int64_t ldw = round_up(d_i, 4), lde = 128, ldr = round_up(d_i, 4);
@@ -263,6 +267,8 @@ int qz_admmq(const float* V, const float* Lambda, const float* sigma, const void
     return fail(QZ_EINVAL, "admmq: null pointer");
   const size_t need = admm_ws(d_o, d_i, grid->group_size, p->iters);
   if (ws_bytes < need || !ws) return fail(QZ_EWORKSPACE, "admmq: workspace too small");
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0)
+    return fail(QZ_EWORKSPACE, "admmq: workspace must be 256-byte aligned");
   set_error("");
   if (d_o == 0) return QZ_OK;
 

@@ -282,18 +282,34 @@ __global__ __launch_bounds__(kThreads) void init_m_kernel(const uint8_t* __restr
   }
 }
 
+// One workgroup per iteration: the per-block partial sums are added in a fixed order
+// (strided per thread, then a tree in LDS), so the result does not depend on timing.
 __global__ __launch_bounds__(kThreads) void residual_kernel(const double* __restrict__ partial,
                                                             int iters, int nblocks,
                                                             float* __restrict__ residuals,
                                                             uint32_t* __restrict__ flag) {
-  for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < iters; t += gridDim.x * blockDim.x) {
-    double sp = 0.0, sd = 0.0;
-    const double* q = partial + static_cast<int64_t>(t) * nblocks * 2;
-    for (int b = 0; b < nblocks; ++b) {
-      sp += q[2 * b];
-      sd += q[2 * b + 1];
+  __shared__ double sp_s[kThreads], sd_s[kThreads];
+  const int t = blockIdx.x;
+  if (t >= iters) return;
+  const double2* q = reinterpret_cast<const double2*>(partial + static_cast<int64_t>(t) * nblocks * 2);
+  double sp = 0.0, sd = 0.0;
+  for (int b = threadIdx.x; b < nblocks; b += kThreads) {
+    const double2 v = q[b];
+    sp += v.x;
+    sd += v.y;
+  }
+  sp_s[threadIdx.x] = sp;
+  sd_s[threadIdx.x] = sd;
+  __syncthreads();
+  for (int h = kThreads / 2; h > 0; h >>= 1) {
+    if (threadIdx.x < h) {
+      sp_s[threadIdx.x] += sp_s[threadIdx.x + h];
+      sd_s[threadIdx.x] += sd_s[threadIdx.x + h];
     }
-    const float rp = static_cast<float>(sqrt(sp)), rd = static_cast<float>(sqrt(sd));
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const float rp = static_cast<float>(sqrt(sp_s[0])), rd = static_cast<float>(sqrt(sd_s[0]));
     if (residuals) {
       residuals[2 * t] = rp;
       residuals[2 * t + 1] = rd;
@@ -356,8 +372,10 @@ int admm_proj_blocks() { return kProjBlocks; }
 
 int launch_admm_project(const AdmmProj& p, hipStream_t s, const float* inv_sigma) {
   // register-resident path when a group is exactly 64, 128 or 256 columns and every row
-  // start is aligned for the vector loads
-  const bool al = (p.d_i % 4 == 0) && (p.ldw % 4 == 0) && (p.ldm % 4 == 0);
+  // start is aligned for the vector loads (U and codes may be the caller's buffers)
+  const bool al = (p.d_i % 4 == 0) && (p.ldw % 4 == 0) && (p.ldm % 4 == 0) &&
+                  (reinterpret_cast<uintptr_t>(p.U) % 16 == 0) &&
+                  (reinterpret_cast<uintptr_t>(p.codes) % 4 == 0);
   if (al && p.group == 128)
     project_reg_kernel<2><<<kProjBlocks, kThreads, 0, s>>>(p, inv_sigma);
   else if (al && p.group == 256)
@@ -381,7 +399,7 @@ int launch_admm_init_m(const uint8_t* codes, const float* scales, const uint8_t*
 int launch_admm_residuals(const double* partial, int iters, int nblocks, float* residuals,
                           uint32_t* flag, hipStream_t s) {
   if (iters <= 0) return QZ_OK;
-  residual_kernel<<<static_cast<unsigned>(ceil_div(iters, kThreads)), kThreads, 0, s>>>(
+  residual_kernel<<<static_cast<unsigned>(iters), kThreads, 0, s>>>(
       partial, iters, nblocks, residuals, flag);
   return check_launch("admm_residuals");
 }

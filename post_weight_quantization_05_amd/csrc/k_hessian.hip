@@ -41,6 +41,7 @@ struct HArgs {
   int64_t S;            // token splits
   int64_t chunk;        // tokens per split (multiple of HBK)
   float* partial;       // [S][n_tiles][HT][HT]
+  int vec;              // rows of X start on 16-byte boundaries (d % 8 == 0, X aligned)
 };
 
 // 16-byte load of 8 channels of one token row (zero outside the matrix).
@@ -99,7 +100,7 @@ __global__ __launch_bounds__(kThreads, 1) void gram_bf16_kernel(const HArgs g) {
   const int64_t k_begin = split * g.chunk;
   int64_t k_end = k_begin + g.chunk;
   if (k_end > g.n) k_end = g.n;
-  const bool vec_ok = (g.d % 8) == 0;
+  const bool vec_ok = g.vec != 0;
 
   // Copy roles: a stage is HBK tokens x 256 channels per panel = 1024 chunks of 16 B;
   // threads take 2 chunks of A and 2 of B (diagonal tiles: B is A and is not copied).
@@ -503,11 +504,12 @@ int hessian_build(const void* X, int xt, int64_t n, int64_t d, float damp, uint3
     g.S = p.S;
     g.chunk = p.chunk;
     g.partial = reinterpret_cast<float*>(static_cast<char*>(ws) + p.tiles_bytes);
+    g.vec = (d % 8 == 0) && (reinterpret_cast<uintptr_t>(X) % 16 == 0);
     schedule_kernel<<<1, 64, 0, s>>>(p.T, const_cast<int32_t*>(g.tiles));
     QZ_TRY(check_launch("gram_schedule"));
     {
       ScopedTimer tm(K_HESSIAN_GRAM, s);
-      if (d % 8 == 0)
+      if (g.vec)
         gram_bf16_dma_kernel<<<static_cast<unsigned>(p.n_tiles * p.S), kThreads, 0, s>>>(g);
       else
         gram_bf16_kernel<<<static_cast<unsigned>(p.n_tiles * p.S), kThreads, 0, s>>>(g);
