@@ -58,10 +58,15 @@ def w_update_eig(P, M, V, lam, rho):
     return ((P + rho * (M @ V)) / (lam + rho)[None, :]) @ V.T
 
 
-def w_update_solve(Ht, Wt_hat, M, rho):
-    """The definition: W~ (H~ + rho I) = W~_hat H~ + rho M, solved directly."""
-    A = Ht + rho * np.eye(Ht.shape[0])
-    return np.linalg.solve(A, (Wt_hat @ Ht + rho * M).T).T
+def w_update_solve(Ht, Wt_hat, M, rho, WtH=None):
+    """The definition: W~ (H~ + rho I) = W~_hat H~ + rho M, solved directly (the matrix
+    is symmetric positive definite: Cholesky).  WtH: W~_hat H~ if already formed."""
+    from scipy.linalg import cho_factor, cho_solve
+    A = np.array(Ht, np.float64)
+    A[np.diag_indices_from(A)] += rho
+    rhs = (Wt_hat @ Ht if WtH is None else WtH) + rho * M
+    return cho_solve(cho_factor(A, lower=True, overwrite_a=True, check_finite=False), rhs.T,
+                     check_finite=False).T
 
 
 def initial_grid(W_hat_f32: np.ndarray, bits: int, group: int):
@@ -74,19 +79,35 @@ def initial_grid(W_hat_f32: np.ndarray, bits: int, group: int):
 
 def admm(H, W_hat_f32, bits, group, iters, rho0, gamma, refresh_every=1, *,
          refresh="clamped", dual="lagrange", state=None, hints=None, zero_hints=None,
-         tol=1e-4, spec=None, trace=False):
+         tol=1e-4, spec=None, trace=False, wupdate="eig"):
     """Run ADMM-Q on the rows of W_hat (fp32 [rows x d_i]; rows are independent, so any
     subset of a layer's rows can be run on its own).
 
     state: warm start dict(t0, codes, scale, zero, U) from an earlier call.
     hints / zero_hints: per-iteration codes [rows x d_i] / zero points [rows x G]
       (indexed by t - t0), used only at near-boundary elements.
+    wupdate: "eig" (the eigendecomposition form) or "solve" (a Cholesky solve of
+      (H~ + rho_t I) per iteration; no eigendecomposition, for short runs on large H).
+      spec: (sigma, H~, Lambda, V) if already computed ("solve" uses sigma and H~ only).
     Returns dict(codes, scale, zero, U, res [iters x 2], adopted, trace)."""
     W_hat_f32 = np.asarray(W_hat_f32, F32)
     rows, d_i = W_hat_f32.shape
-    sig, Ht, lam, V = spec if spec is not None else spectral(H)
+    if wupdate == "eig":
+        sig, Ht, lam, V = spec if spec is not None else spectral(H)
+    elif wupdate == "solve":
+        if spec is not None:
+            sig, Ht = spec[0], spec[1]
+        else:
+            Hd = np.asarray(H, np.float64)
+            sig = 1.0 / np.sqrt(np.diag(Hd))
+            Ht = Hd * sig[:, None] * sig[None, :]
+    else:
+        raise ValueError(f"unknown wupdate {wupdate!r}")
     Wt_hat = W_hat_f32.astype(np.float64) / sig[None, :]
-    P = (Wt_hat @ V) * lam[None, :]
+    if wupdate == "eig":
+        P = (Wt_hat @ V) * lam[None, :]
+    else:
+        WtH = Wt_hat @ Ht
     lo0, hi0, s0, z0, c0 = initial_grid(W_hat_f32, bits, group)
     if state is None:
         t0, C, scale, zero, U = 0, c0.astype(np.int64), s0, z0.astype(np.int64), np.zeros((rows, d_i))
@@ -105,7 +126,10 @@ def admm(H, W_hat_f32, bits, group, iters, rho0, gamma, refresh_every=1, *,
         rho_next = rho0 * gamma ** (t + 1)
         Dt = dequant(C, scale, zero, group) / sig[None, :]
         M = Dt - U
-        Wt = w_update_eig(P, M, V, lam, rho)
+        if wupdate == "eig":
+            Wt = w_update_eig(P, M, V, lam, rho)
+        else:
+            Wt = w_update_solve(Ht, Wt_hat, M, rho, WtH)
         if refresh_every > 0 and t % refresh_every == 0 and refresh != "off":
             src = (Wt + U) * sig[None, :] if refresh == "from_z" else Wt * sig[None, :]
             lo, hi = fit_range_f64(src, group)

@@ -33,6 +33,27 @@ def inverse_factor(H: np.ndarray) -> np.ndarray:
     return np.linalg.cholesky(Hinv).T
 
 
+def inverse_factor_lapack(H: np.ndarray) -> np.ndarray:
+    """The same R as inverse_factor (invert, then the upper Cholesky factor of the
+    inverse), through LAPACK's symmetric positive-definite drivers: H = U^T U (potrf),
+    H^{-1} from U (potri), then R^T R = H^{-1} (potrf).  About a third of the general
+    inverse's work, for layers with tens of thousands of input channels."""
+    from scipy.linalg import lapack
+    A = np.array(H, np.float64, order="F")
+    U, info = lapack.dpotrf(A, lower=0, clean=1, overwrite_a=1)
+    if info != 0:
+        raise np.linalg.LinAlgError(f"H is not positive definite (potrf info {info})")
+    Hinv, info = lapack.dpotri(U, lower=0, overwrite_c=1)
+    if info != 0:
+        raise np.linalg.LinAlgError(f"potri info {info}")
+    iu = np.triu_indices_from(Hinv, 1)
+    Hinv[(iu[1], iu[0])] = Hinv[iu]
+    R, info = lapack.dpotrf(Hinv, lower=0, clean=1, overwrite_a=1)
+    if info != 0:
+        raise np.linalg.LinAlgError(f"H^-1 is not positive definite (potrf info {info})")
+    return np.ascontiguousarray(R)
+
+
 def _column_grid(scale, zero, group, col):
     g = col // group
     return np.asarray(scale[:, g], np.float64), np.asarray(zero[:, g], np.float64)

@@ -170,3 +170,19 @@ WORKLOADS = {
                                       iters=200, rho0=0.05, gamma=1.05, refresh=10, damp=0.01,
                                       p_out=0.005, f_out=50.0, seed=5),
 }
+
+
+# ---------------------------------------------------------------- decoder block
+# One 8B-like decoder block quantized sub-layer by sub-layer: (name, input, d_i, d_o,
+# weight seed).  Inputs: x0 = calibration tokens; x_attn = v_proj's output with its 8
+# heads of 128 channels each repeated 4 times; x_mlp = o_proj's output; x_down =
+# up_proj's output.  q/k/v share x0's Hessian and gate/up share x_mlp's.
+BLOCK_8B = dict(
+    n=262144, d_model=4096, d_ff=12288, kv_heads=8, head_dim=128, q_heads=32,
+    calib_seed=6, p_out=0.01, f_out=30.0, damp=0.01, group=128, B=128,
+    iters=100, rho0=0.05, gamma=1.05, refresh=1,
+    sublayers=[("q_proj", "x0", 4096, 4096, 11), ("k_proj", "x0", 4096, 1024, 12),
+               ("v_proj", "x0", 4096, 1024, 13), ("o_proj", "x_attn", 4096, 4096, 14),
+               ("gate_proj", "x_mlp", 4096, 12288, 15), ("up_proj", "x_mlp", 4096, 12288, 16),
+               ("down_proj", "x_down", 12288, 4096, 17)],
+)

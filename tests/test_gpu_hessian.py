@@ -7,27 +7,11 @@ import pytest
 
 import qz_synth
 from gpu_util import qz, report, to_dev, to_host
+from layer_parity import U32
+from layer_parity import check_hessian as _check
 from oracle import hessian
 
 pytestmark = pytest.mark.gpu
-U32 = 2.0 ** -24
-
-
-def _check(H, G, n, lam_gpu, damp, diag=None, sigma=None):
-    d = G.shape[0]
-    lam = damp * np.mean(np.diag(G))
-    assert abs(lam_gpu - lam) <= 1e-5 * lam + 1e-30
-    ref = G + lam * np.eye(d)
-    g = np.sqrt(np.outer(np.diag(G), np.diag(G)))
-    err = np.abs(H.astype(np.float64) - ref)
-    tol = 4 * U32 * np.sqrt(max(n, 1)) * g + 1e-30
-    worst = float((err / tol).max())
-    assert worst <= 1.0, worst
-    np.testing.assert_array_equal(H, H.T)
-    if diag is not None:
-        np.testing.assert_array_equal(diag, np.diag(H))
-        np.testing.assert_array_equal(sigma, np.float32(1) / np.sqrt(diag))
-    return worst
 
 
 @pytest.mark.parametrize("n,d", [(3000, 200), (512, 128), (4096, 77), (64, 8), (130, 300)])

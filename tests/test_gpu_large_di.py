@@ -1,0 +1,70 @@
+"""GPU parity for the layers with many input channels, at full shape, in the
+benchmark's launch configuration, on sampled rows: the MLP down projection
+12288 -> 4096 (W2 g128, 150 ADMM-Q iterations) and the 32B-like down projection
+25600 -> 5120 (W3 g128, 200 iterations, grid refresh every 10).
+
+H is the oracle's, from the first 8192 calibration tokens of the layer's own input
+recipe plus the damping (a full-token fp64 sum over 262144 tokens would take many
+minutes on the host; with fewer tokens than channels the damping keeps H positive
+definite).  The GPU's full-token Hessian is checked in test_gpu_hessian.py.
+
+GPTQ: whole sampled rows against the oracle, R from LAPACK's SPD drivers.
+ADMM-Q: the iteration map (one iteration from the initial state, and from the state
+the GPU reached at later t), because a fp64 eigendecomposition of H at these sizes is
+beyond a test's time on the host.
+"""
+import numpy as np
+import pytest
+
+import qz_synth
+from gpu_util import to_host
+from layer_parity import admm_rows_replay, gptq_rows, oracle_hessian, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+N_ORACLE_TOKENS = 8192
+LAYERS = ["mlp_down_12288x4096_w2g128", "32b_down_25600x5120_w3g128"]
+_cache = {}
+
+
+def _layer(name):
+    """(cfg, Hf fp32, W bits) for one layer; only the most recent layer is kept."""
+    if name not in _cache:
+        _cache.clear()
+        import torch
+        cfg = qz_synth.WORKLOADS[name]
+        X = qz_synth.calib_bf16_torch(cfg["seed"], N_ORACLE_TOKENS, cfg["d_i"], cfg["p_out"],
+                                      cfg["f_out"])
+        Xh = to_host(X)
+        del X
+        torch.cuda.empty_cache()
+        H, Hf = oracle_hessian(Xh, cfg["damp"])
+        del H, Xh
+        W = qz_synth.weights_bf16(cfg["seed"], cfg["d_o"], cfg["d_i"])
+        _cache[name] = dict(cfg=cfg, Hf=Hf, W=W, f_gptq=None)
+    return _cache[name]
+
+
+def _replay_points(cfg):
+    T, k = cfg["iters"], cfg["refresh"]
+    last_refresh = (T - 1) // k * k
+    return sorted({0, last_refresh, T - 1})
+
+
+@pytest.mark.parametrize("name", LAYERS)
+def test_gptq_large_di_sampled_rows(name):
+    L = _layer(name)
+    cfg = L["cfg"]
+    rows = sample_rows(cfg["d_o"])
+    _, f_ref = gptq_rows(name, L["Hf"], L["W"], rows, cfg["bits"], cfg["group"], cfg["B"])
+    L["f_gptq"] = f_ref
+
+
+@pytest.mark.parametrize("name", LAYERS)
+def test_admm_large_di_iteration_map(name):
+    L = _layer(name)
+    cfg = L["cfg"]
+    rows = sample_rows(cfg["d_o"])
+    admm_rows_replay(name, L["Hf"], L["W"], rows, cfg["bits"], cfg["group"], cfg["iters"],
+                     cfg["rho0"], cfg["gamma"], cfg["refresh"], _replay_points(cfg),
+                     f_gptq=L["f_gptq"])

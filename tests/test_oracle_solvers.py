@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 import scipy.linalg
 
+import qz_synth
 from conftest import golden
 from oracle import admm, gptq, grid, hessian, lattice, objective
 
@@ -108,6 +109,21 @@ def test_gptq_worked_example_collinear_needs_damping():
 
 
 # ------------------------------------------------------------------ GPTQ routes
+def test_inverse_factor_lapack_is_the_same_factor():
+    # the LAPACK route (potrf, potri, potrf) is the definition's R: upper, positive
+    # diagonal, R^T R H = I, and equal to the general-inverse route
+    rng = np.random.default_rng(7)
+    for d in (1, 9, 64, 131):
+        _, H = spd(d, rng, cond_scale=30.0)
+        R = gptq.inverse_factor_lapack(H)
+        np.testing.assert_array_equal(np.tril(R, -1), 0)
+        assert np.all(np.diag(R) > 0)
+        np.testing.assert_allclose(R.T @ R @ H, np.eye(d), atol=1e-8)
+        np.testing.assert_allclose(R, gptq.inverse_factor(H), rtol=1e-8, atol=1e-10)
+    with pytest.raises(np.linalg.LinAlgError):
+        gptq.inverse_factor_lapack(-np.eye(3))
+
+
 @pytest.mark.parametrize("B", [1, 3, 16, 40])
 @pytest.mark.parametrize("clip", [True, False])
 def test_gptq_blocked_equals_lagrange_route(B, clip):
@@ -307,6 +323,28 @@ def test_admm_w_update_eig_equals_solve():
     for rho in (1e-3, 0.05, 3.0):
         np.testing.assert_allclose(admm.w_update_eig(P, M, V, lam, rho),
                                    admm.w_update_solve(Ht, Wt_hat, M, rho), rtol=1e-9, atol=1e-12)
+
+
+@pytest.mark.parametrize("refresh_every", [1, 3])
+def test_admm_solve_route_follows_the_eig_route(refresh_every):
+    # the Cholesky-solve W-update gives the same trajectory as the eigendecomposition
+    # form, also when started from a mid-run state (single-step replay)
+    X, W, _ = qz_synth.tiny_layer(3)
+    H, _ = hessian.hessian(X, 0.01)
+    W = W[:16]
+    a = admm.admm(H, W, 4, 128, 12, 0.1, 1.3, refresh_every, trace=True)
+    b = admm.admm(H, W, 4, 128, 12, 0.1, 1.3, refresh_every, wupdate="solve")
+    np.testing.assert_array_equal(a["codes"], b["codes"])
+    np.testing.assert_array_equal(a["zero"], b["zero"])
+    np.testing.assert_allclose(a["scale"], b["scale"], rtol=1e-6)
+    np.testing.assert_allclose(a["U"], b["U"], rtol=1e-7, atol=1e-9)
+    mid = admm.admm(H, W, 4, 128, 7, 0.1, 1.3, refresh_every)
+    st = dict(t0=7, codes=mid["codes"], scale=mid["scale"], zero=mid["zero"], U=mid["U"])
+    c = admm.admm(H, W, 4, 128, 5, 0.1, 1.3, refresh_every, state=st, wupdate="solve")
+    np.testing.assert_array_equal(c["codes"], a["codes"])
+    np.testing.assert_allclose(c["U"], a["U"], rtol=1e-7, atol=1e-9)
+    with pytest.raises(ValueError):
+        admm.admm(H, W, 4, 128, 1, 0.1, 1.3, wupdate="lu")
 
 
 def test_admm_w_update_is_penalised_minimiser():
