@@ -55,83 +55,75 @@ __global__ __launch_bounds__(kThreads) void init_reversed(const float* __restric
 }
 
 // Factor diagonal block k in place (lower) and write its inverse to Dinv[k].
-__global__ __launch_bounds__(kThreads) void diag_block(double* __restrict__ A, int64_t lda, int64_t k,
-                                                       const double* __restrict__ diag0,
-                                                       double* __restrict__ Dinv,
-                                                       uint32_t* __restrict__ flag) {
-  __shared__ double a[NB][NB + 1];
-  __shared__ double x[NB][NB + 1];
-  const int tid = threadIdx.x;
+// One wavefront: lane i holds row i of the block in registers during the factorisation
+// (column j is scaled by the pivot's reciprocal square root, written to LDS and read
+// back by every lane as uniform broadcasts for the rank-one update of the rows below),
+// and column i of the inverse during the forward substitution (rows of L come from LDS
+// as uniform reads, the diagonal's reciprocals are formed up front).  All exchanges
+// stay within the wavefront.
+__global__ __launch_bounds__(NB) void diag_block(double* __restrict__ A, int64_t lda, int64_t k,
+                                                 const double* __restrict__ diag0,
+                                                 double* __restrict__ Dinv,
+                                                 uint32_t* __restrict__ flag) {
+  __shared__ double Ls[NB][NB + 2];   // rows of L (even stride: 16-byte pair reads)
+  __shared__ double rinv[NB];
+  const int i = threadIdx.x;
   const int64_t k0 = k * NB;
-  for (int e = tid; e < NB * NB; e += kThreads) {
-    const int i = e / NB, j = e % NB;
-    a[i][j] = A[(k0 + i) * lda + k0 + j];
-    x[i][j] = (i == j) ? 1.0 : 0.0;
-  }
-  __syncthreads();
+  double a[NB];
+  const double* __restrict__ row = A + (k0 + i) * lda + k0;
+#pragma unroll
+  for (int c = 0; c < NB; ++c) a[c] = (c <= i) ? row[c] : 0.0;
+  const double tol = 1e-12 * diag0[k0 + i];
   bool notpd = false;
-  // unblocked right-looking Cholesky of the lower triangle
+#pragma unroll
   for (int j = 0; j < NB; ++j) {
-    const double p = a[j][j];
-    const double tol = 1e-12 * diag0[k0 + j];
-    if (!(p > tol) || !__builtin_isfinite(p)) notpd = true;
-    const double ljj = sqrt(p > 0.0 ? p : 0.0);
-    __syncthreads();
-    if (tid == 0) a[j][j] = ljj;
-    for (int i = j + 1 + tid; i < NB; i += kThreads) a[i][j] = a[i][j] / ljj;
-    __syncthreads();
-    // trailing update a[i][l] -= a[i][j] a[l][j], j < l <= i
-    const int m = NB - j - 1;
-    for (int e = tid; e < m * m; e += kThreads) {
-      const int i = j + 1 + e / m, l = j + 1 + e % m;
-      if (l <= i) a[i][l] -= a[i][j] * a[l][j];
+    // lane j publishes its pivot; every lane reads it back
+    if (i == j) {
+      const double p = a[j];
+      notpd = !(p > tol) || !__builtin_isfinite(p);
+      const double r = 1.0 / sqrt(p > 0.0 ? p : 0.0);
+      rinv[j] = r;
     }
-    __syncthreads();
-  }
-  if (notpd && tid == 0) atomicOr(flag, FLAG_NOTPD);
-  // inverse of the lower factor by forward substitution on all columns at once:
-  // row i of X = (row i of B - sum_{p<i} L[i][p] X[p]) / L[i][i], done right-looking.
-  for (int i = 0; i < NB; ++i) {
-    const double inv = 1.0 / a[i][i];
-    for (int c = tid; c <= i; c += kThreads) x[i][c] *= inv;
-    __syncthreads();
-    const int m = NB - i - 1;
-    for (int e = tid; e < m * (i + 1); e += kThreads) {
-      const int r = i + 1 + e / (i + 1), c = e % (i + 1);
-      x[r][c] -= a[r][i] * x[i][c];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    const double r = rinv[j];
+    const double lij = (i > j) ? a[j] * r : ((i == j) ? a[j] * r : 0.0);
+    a[j] = lij;
+    Ls[i][j] = lij;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    // a[i][l] -= L[i][j] L[l][j] for j < l <= i
+#pragma unroll
+    for (int l = j + 1; l < NB; ++l) {
+      const double llj = Ls[l][j];
+      if (i >= l) a[l] = fma(-lij, llj, a[l]);
     }
-    __syncthreads();
   }
-  for (int e = tid; e < NB * NB; e += kThreads) {
-    const int i = e / NB, j = e % NB;
-    if (j <= i) A[(k0 + i) * lda + k0 + j] = a[i][j];
-    Dinv[k * NB * NB + e] = (j <= i) ? x[i][j] : 0.0;
+  if (notpd) atomicOr(flag, FLAG_NOTPD);
+#pragma unroll
+  for (int c = 0; c < NB; ++c)
+    if (c <= i) A[(k0 + i) * lda + k0 + c] = a[c];
+  // Ls holds L (lower; entries above the diagonal are zero); rinv[r] = 1 / L[r][r]
+  // X = L^{-1}, lane i holds column i: x[r] = (delta_ri - sum_{q<r} L[r][q] x[q]) / L[r][r]
+  double x[NB];
+#pragma unroll
+  for (int r = 0; r < NB; ++r) {
+    double acc = (r == i) ? 1.0 : 0.0;
+#pragma unroll
+    for (int q = 0; q < r; ++q) acc = fma(-Ls[r][q], x[q], acc);
+    x[r] = acc * rinv[r];
   }
+  double* __restrict__ out = Dinv + k * NB * NB;
+#pragma unroll
+  for (int r = 0; r < NB; ++r) out[r * NB + i] = (r >= i) ? x[r] : 0.0;
 }
 
 // Rows below block k:  A[i][k-block] <- A[i][k-block] * Dinv_k^T.  One 64-row tile
 // per workgroup.
 __global__ __launch_bounds__(kThreads) void panel_solve(double* __restrict__ A, int64_t lda, int64_t k,
-                                                        const double* __restrict__ Dinv) {
-  __shared__ double p[NB][NB + 1];
-  __shared__ double dv[NB][NB + 1];
-  const int tid = threadIdx.x;
-  const int64_t k0 = k * NB;
-  const int64_t r0 = k0 + NB + static_cast<int64_t>(blockIdx.x) * NB;
-  for (int e = tid; e < NB * NB; e += kThreads) {
-    const int i = e / NB, j = e % NB;
-    p[i][j] = A[(r0 + i) * lda + k0 + j];
-    dv[i][j] = Dinv[k * NB * NB + e];
-  }
-  __syncthreads();
-  // out[i][c] = sum_{q <= c} p[i][q] * Dinv[c][q]
-  for (int e = tid; e < NB * NB; e += kThreads) {
-    const int i = e / NB, c = e % NB;
-    double s = 0.0;
-    for (int q = 0; q <= c; ++q) s += p[i][q] * dv[c][q];
-    A[(r0 + i) * lda + k0 + c] = s;
-  }
-}
+                                                        const double* __restrict__ Dinv);
 
 __device__ __forceinline__ void tri_tile(int64_t t, int64_t& ti, int64_t& tj) {
   // lower-triangle enumeration: (0,0), (1,0), (1,1), (2,0), ...
@@ -142,11 +134,12 @@ __device__ __forceinline__ void tri_tile(int64_t t, int64_t& ti, int64_t& tj) {
   tj = t - i * (i + 1) / 2;
 }
 
-// C[64x64 tile] -= A_op * B_op with K = 64.
+// C[64x64 tile] -= A_op * B_op (STORE: C = A_op * B_op) with K = 64.
 //  A_op[m][q] = A[(am0 + m) * lda + ak0 + q]
 //  B_op[q][n] = BNN ? B[(bk0 + q) * ldb + bn0 + n] : B[(bn0 + n) * ldb + bk0 + q]
+// Both operands are staged in LDS before any output is written, so C may alias them.
 // Threads own 4 x 4 outputs (rows ty + 16a, cols tx + 16b).
-template <bool BNN>
+template <bool BNN, bool STORE = false>
 __device__ __forceinline__ void tile_update(double* __restrict__ C, int64_t ldc, int64_t cm0,
                                             int64_t cn0, const double* __restrict__ A, int64_t lda,
                                             int64_t am0, int64_t ak0, const double* __restrict__ B,
@@ -183,8 +176,19 @@ __device__ __forceinline__ void tile_update(double* __restrict__ C, int64_t ldc,
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       double* c = C + (cm0 + ty + 16 * a) * ldc + cn0 + tx + 16 * b;
-      *c -= acc[a][b];
+      if (STORE)
+        *c = acc[a][b];
+      else
+        *c -= acc[a][b];
     }
+}
+
+__global__ __launch_bounds__(kThreads) void panel_solve(double* __restrict__ A, int64_t lda, int64_t k,
+                                                        const double* __restrict__ Dinv) {
+  const int64_t k0 = k * NB;
+  const int64_t r0 = k0 + NB + static_cast<int64_t>(blockIdx.x) * NB;
+  // out[i][c] = sum_q A[r0+i][k0+q] Dinv_k[c][q]
+  tile_update<false, true>(A, lda, r0, k0, A, lda, r0, k0, Dinv + k * NB * NB, NB, 0, 0);
 }
 
 // Cholesky trailing update after block column k: lower tiles (ti >= tj) of the
@@ -200,22 +204,8 @@ __global__ __launch_bounds__(kThreads) void chol_trailing(double* __restrict__ A
 // Inverse step i, part 1: X[i][j-block] = Dinv_i * S[i][j-block] for j <= i, in place.
 __global__ __launch_bounds__(kThreads) void inv_rowscale(double* __restrict__ X, int64_t ldx, int64_t i,
                                                          const double* __restrict__ Dinv) {
-  __shared__ double s[NB][NB + 1];
-  __shared__ double dv[NB][NB + 1];
-  const int tid = threadIdx.x;
   const int64_t r0 = i * NB, c0 = static_cast<int64_t>(blockIdx.x) * NB;
-  for (int e = tid; e < NB * NB; e += kThreads) {
-    const int r = e / NB, c = e % NB;
-    s[r][c] = X[(r0 + r) * ldx + c0 + c];
-    dv[r][c] = Dinv[i * NB * NB + e];
-  }
-  __syncthreads();
-  for (int e = tid; e < NB * NB; e += kThreads) {
-    const int r = e / NB, c = e % NB;
-    double acc = 0.0;
-    for (int q = 0; q <= r; ++q) acc += dv[r][q] * s[q][c];
-    X[(r0 + r) * ldx + c0 + c] = acc;
-  }
+  tile_update<true, true>(X, ldx, r0, c0, Dinv + i * NB * NB, NB, 0, 0, X, ldx, r0, c0);
 }
 
 // Inverse step i, part 2: S[r][j] -= L[r][i] X[i][j] for block rows r > i, j <= i.
@@ -279,7 +269,7 @@ int rfactor(const float* H, int64_t d, const int32_t* perm, float* Rt, int64_t l
   init_reversed<<<grid_for(dp * dp), kThreads, 0, s>>>(H, d, perm, A, dp, diag0, flag);
   QZ_TRY(check_launch("rfactor.init"));
   for (int64_t k = 0; k < nblk; ++k) {
-    diag_block<<<1, kThreads, 0, s>>>(A, dp, k, diag0, Dinv, flag);
+    diag_block<<<1, NB, 0, s>>>(A, dp, k, diag0, Dinv, flag);
     QZ_TRY(check_launch("rfactor.diag"));
     const int64_t below = nblk - k - 1;
     if (below > 0) {
