@@ -27,7 +27,14 @@ namespace qz {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kProjBlocks = 16384;   // many resident waves: more bytes in flight
+// Wavefronts of the projection launch: about 131072 (32768 workgroups, many bytes in
+// flight), rounded to a multiple of the number of groups per row so that every
+// wavefront keeps one column group and strides over rows.
+constexpr int64_t kProjWaves = 131072;
+__host__ __device__ inline int64_t proj_waves(int64_t G) {
+  const int64_t per = kProjWaves / G;
+  return (per > 0 ? per : 1) * G;
+}
 
 __global__ __launch_bounds__(kThreads) void project_kernel(const AdmmProj p,
                                                            const float* __restrict__ inv_sigma) {
@@ -156,42 +163,63 @@ __device__ __forceinline__ void cstore(uint8_t* p, const uint8_t (&c)[EPL]) {
   *reinterpret_cast<C*>(p) = x;
 }
 
+// Min and max over the 64 lanes with DPP moves (VALU latency, no LDS round trips): quad
+// swaps, half-row and row mirrors, then the row broadcasts; lane 63 ends with the
+// result, which is read back as a uniform value.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_move(float v) {
+  const int x = __builtin_bit_cast(int, v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(x, x, CTRL, ROW_MASK, 0xF, false));
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ void minmax_step(float& lo, float& hi) {
+  lo = fminf(lo, dpp_move<CTRL, ROW_MASK>(lo));
+  hi = fmaxf(hi, dpp_move<CTRL, ROW_MASK>(hi));
+}
+__device__ __forceinline__ void wave_minmax(float& lo, float& hi) {
+  minmax_step<0xB1>(lo, hi);         // quad_perm [1,0,3,2]
+  minmax_step<0x4E>(lo, hi);         // quad_perm [2,3,0,1]
+  minmax_step<0x141>(lo, hi);        // row_half_mirror
+  minmax_step<0x140>(lo, hi);        // row_mirror
+  minmax_step<0x142, 0xA>(lo, hi);   // row_bcast:15 into rows 1 and 3
+  minmax_step<0x143, 0xC>(lo, hi);   // row_bcast:31 into rows 2 and 3
+  lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lo), 63));
+  hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, hi), 63));
+}
+
+// Register-resident variant for groups of exactly 64*EPL columns (64, 128, 256): lane l
+// owns EPL consecutive columns of the group and loads them once with vector loads (the
+// min/max of the refresh comes from the registers, no second pass over memory).  Each
+// wavefront keeps one column group (Sigma loaded once) and strides over the rows.  The
+// code is rint(x * (1/s)) with the correctly rounded reciprocal of s: it can differ from
+// rint(x / s) only where x / s lies within an ulp of a rounding boundary.  Residual
+// terms are summed per lane in fp32 over the wavefront's few rows, then in fp64.
 template <int EPL>
 __global__ __launch_bounds__(kThreads) void project_reg_kernel(const AdmmProj p,
                                                                const float* __restrict__ inv_sigma) {
-  constexpr int UNR = 1;
   __shared__ double red[kThreads / 64][2];
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
   const int64_t G = p.d_i / p.group;
-  const int64_t total = p.d_o * G;
+  const int64_t nwaves = proj_waves(G);
+  const int64_t w = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + wid;
   const float maxq = static_cast<float>((1 << p.bits) - 1);
-  const int64_t wstride = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
   const float rs = p.rescale ? p.rho / p.rho_next : 1.0f;
-  double acc_p = 0.0, acc_d = 0.0;
-
-  for (int64_t t0 = (blockIdx.x * (kThreads / 64) + wid) * UNR; t0 < total; t0 += wstride * UNR) {
-    float w[UNR][EPL], u[UNR][EPL], sg[UNR][EPL], isg[UNR][EPL];
-    uint8_t cd[UNR][EPL];
-    int64_t rr[UNR], cc[UNR];
-    bool live[UNR];
-#pragma unroll
-    for (int k = 0; k < UNR; ++k) {
-      const int64_t t = t0 + k;
-      live[k] = t < total;
-      const int64_t tt = live[k] ? t : t0;
-      rr[k] = tt / G;
-      cc[k] = (tt % G) * p.group + lane * EPL;
-      vload<EPL>(p.Wt + rr[k] * p.ldw + cc[k], w[k]);
-      vload<EPL>(p.U + rr[k] * p.d_i + cc[k], u[k]);
-      vload<EPL>(p.sigma + cc[k], sg[k]);
-      vload<EPL>(inv_sigma + cc[k], isg[k]);
-      cload<EPL>(p.codes + rr[k] * p.d_i + cc[k], cd[k]);
-    }
-#pragma unroll
-    for (int k = 0; k < UNR; ++k) {
-      if (!live[k]) continue;   // wave-uniform
-      const int64_t t = t0 + k;
+  float sum_p = 0.f, sum_d = 0.f;
+  if (w < nwaves) {
+    const int64_t gc = w % G;
+    const int64_t rstep = nwaves / G;
+    const int64_t cc = gc * p.group + lane * EPL;
+    float sg[EPL], isg[EPL];
+    vload<EPL>(p.sigma + cc, sg);
+    vload<EPL>(inv_sigma + cc, isg);
+    for (int64_t r = w / G; r < p.d_o; r += rstep) {
+      const int64_t t = r * G + gc;
+      float wv[EPL], u[EPL];
+      uint8_t cd[EPL];
+      vload<EPL>(p.Wt + r * p.ldw + cc, wv);
+      vload<EPL>(p.U + r * p.d_i + cc, u);
+      cload<EPL>(p.codes + r * p.d_i + cc, cd);
       const float s_old = p.scales[t];
       const float z_old = static_cast<float>(p.zeros[t]);
       float s = s_old, z = z_old;
@@ -199,16 +227,13 @@ __global__ __launch_bounds__(kThreads) void project_reg_kernel(const AdmmProj p,
         float lo = 0.f, hi = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
-          float v = w[k][e];
-          if (p.refresh == 3) v += u[k][e];
-          v *= sg[k][e];
+          float v = wv[e];
+          if (p.refresh == 3) v += u[e];
+          v *= sg[e];
           lo = fminf(lo, v);
           hi = fmaxf(hi, v);
         }
-        for (int off = 32; off > 0; off >>= 1) {
-          lo = fminf(lo, __shfl_xor(lo, off));
-          hi = fmaxf(hi, __shfl_xor(hi, off));
-        }
+        wave_minmax(lo, hi);
         if (hi == lo) { lo = -1.f; hi = 1.f; }
         if (p.refresh != 2) {
           lo = fmaxf(lo, p.lo0[t]);
@@ -217,30 +242,32 @@ __global__ __launch_bounds__(kThreads) void project_reg_kernel(const AdmmProj p,
         s = (hi - lo) / maxq;
         z = fminf(fmaxf(__builtin_rintf(-lo / s), 0.f), maxq);
       }
+      const float rcp = 1.0f / s;
       float un[EPL], mm[EPL];
       uint8_t cn[EPL];
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
-        const float zv = (w[k][e] + u[k][e]) * sg[k][e];
-        const float c = quant_code(zv, s, z, maxq);
-        const float dt = s * (c - z) * isg[k][e];
-        const float dold = s_old * (static_cast<float>(cd[k][e]) - z_old) * isg[k][e];
-        un[e] = (u[k][e] + w[k][e] - dt) * rs;
+        const float zv = (wv[e] + u[e]) * sg[e];
+        const float c = fminf(fmaxf(__builtin_rintf(zv * rcp) + z, 0.f), maxq);
+        const float dt = s * (c - z) * isg[e];
+        const float dold = s_old * (static_cast<float>(cd[e]) - z_old) * isg[e];
+        un[e] = (u[e] + wv[e] - dt) * rs;
         mm[e] = dt - un[e];
         cn[e] = static_cast<uint8_t>(c);
-        const float ep = w[k][e] - dt, ed = dt - dold;
-        acc_p += static_cast<double>(ep) * ep;
-        acc_d += static_cast<double>(ed) * ed;
+        const float ep = wv[e] - dt, ed = dt - dold;
+        sum_p += ep * ep;
+        sum_d += ed * ed;
       }
-      vstore<EPL>(p.U + rr[k] * p.d_i + cc[k], un);
-      vstore<EPL>(p.M + rr[k] * p.ldm + cc[k], mm);
-      cstore<EPL>(p.codes + rr[k] * p.d_i + cc[k], cn);
+      vstore<EPL>(p.U + r * p.d_i + cc, un);
+      vstore<EPL>(p.M + r * p.ldm + cc, mm);
+      cstore<EPL>(p.codes + r * p.d_i + cc, cn);
       if (p.refresh && lane == 0) {
         p.scales[t] = s;
         p.zeros[t] = static_cast<uint8_t>(z);
       }
     }
   }
+  double acc_p = sum_p, acc_d = sum_d;
   for (int off = 32; off > 0; off >>= 1) {
     acc_p += __shfl_xor(acc_p, off);
     acc_d += __shfl_xor(acc_d, off);
@@ -252,9 +279,9 @@ __global__ __launch_bounds__(kThreads) void project_reg_kernel(const AdmmProj p,
   __syncthreads();
   if (threadIdx.x == 0) {
     double sp = 0.0, sd = 0.0;
-    for (int w = 0; w < kThreads / 64; ++w) {
-      sp += red[w][0];
-      sd += red[w][1];
+    for (int k = 0; k < kThreads / 64; ++k) {
+      sp += red[k][0];
+      sd += red[k][1];
     }
     const double rho = p.rho;
     p.partial[2 * blockIdx.x] = sp;
@@ -368,7 +395,7 @@ inline unsigned grid_for(int64_t n) {
 
 }  // namespace
 
-int admm_proj_blocks() { return kProjBlocks; }
+int admm_proj_blocks(int64_t G) { return static_cast<int>(ceil_div(proj_waves(G > 0 ? G : 1), int64_t{kThreads / 64})); }
 
 int launch_admm_project(const AdmmProj& p, hipStream_t s, const float* inv_sigma) {
   // register-resident path when a group is exactly 64, 128 or 256 columns and every row
@@ -376,14 +403,15 @@ int launch_admm_project(const AdmmProj& p, hipStream_t s, const float* inv_sigma
   const bool al = (p.d_i % 4 == 0) && (p.ldw % 4 == 0) && (p.ldm % 4 == 0) &&
                   (reinterpret_cast<uintptr_t>(p.U) % 16 == 0) &&
                   (reinterpret_cast<uintptr_t>(p.codes) % 4 == 0);
+  const int nb = admm_proj_blocks(p.d_i / p.group);
   if (al && p.group == 128)
-    project_reg_kernel<2><<<kProjBlocks, kThreads, 0, s>>>(p, inv_sigma);
+    project_reg_kernel<2><<<nb, kThreads, 0, s>>>(p, inv_sigma);
   else if (al && p.group == 256)
-    project_reg_kernel<4><<<kProjBlocks, kThreads, 0, s>>>(p, inv_sigma);
+    project_reg_kernel<4><<<nb, kThreads, 0, s>>>(p, inv_sigma);
   else if (p.group == 64)
-    project_reg_kernel<1><<<kProjBlocks, kThreads, 0, s>>>(p, inv_sigma);
+    project_reg_kernel<1><<<nb, kThreads, 0, s>>>(p, inv_sigma);
   else
-    project_kernel<<<kProjBlocks, kThreads, 0, s>>>(p, inv_sigma);
+    project_kernel<<<nb, kThreads, 0, s>>>(p, inv_sigma);
   return check_launch("admm_project");
 }
 
