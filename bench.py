@@ -32,6 +32,8 @@ HEADLINE = "up_4096x12288_w3g128"
 PEAK_BF16 = 2.5e15        # dense MFMA, FLOP/s
 PEAK_FP32_MFMA = 157.3e12
 PEAK_HBM = 8.0e12         # B/s
+PEAK_FP32_VALU = 157.3e12  # vector fp32 (packed), FLOP/s
+PEAK_FP64 = 78.6e12        # vector / matrix fp64, FLOP/s
 
 # HBM-side bytes per launch on the headline workload, from two rocprofv3 --pmc runs
 # (FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0, the factors that make a plain 1 GiB streaming
@@ -75,6 +77,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=3072)
     ap.add_argument("--cpu-iters", type=int, default=40)
+    ap.add_argument("--sweep", action="store_true",
+                    help="one line per layer workload (1 warm-up and 1 timed step each), no CPU leg")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain streaming kernel (y = -x over MIB MiB of fp32, 3 launches) "
                          "whose byte counts calibrate the HBM traffic counters, then exit")
@@ -124,21 +128,24 @@ def cpu_baseline(cfg, X, W_bits, rows, iters):
                       f"loop {t_loop:.2f} s, H build {t_h:.2f} s"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the quantizer's rows shard "
-              f"across GPUs without per-iteration exchange, but no multi-GPU path is built.",
-              file=sys.stderr)
-        sys.exit(2)
-    if args.copy_probe:
-        copy_probe(args.copy_probe)
-        return
+def gptq_work(d_o, d_i, B):
+    """flops of the GPTQ loop: the trailing products W[:, b:] -= E R[a:b, b:] summed over
+    blocks, and the in-block column updates."""
+    trailing, inblock = 0.0, 0.0
+    for a in range(0, d_i, B):
+        b = min(a + B, d_i)
+        trailing += 2.0 * d_o * (b - a) * (d_i - b)
+        inblock += 1.0 * d_o * (b - a) * (b - a + 1)
+    return trailing, inblock
+
+
+def run_workload(args, name, steps, warmup, with_cpu):
+    """One bench line for workload `name` (inputs resident in HBM before timing)."""
     import numpy as np
     import torch
     import post_weight_quantization_05_amd as q
 
-    cfg = dict(qz_synth.WORKLOADS[args.workload])
+    cfg = dict(qz_synth.WORKLOADS[name])
     d_i, d_o, n = cfg["d_i"], cfg["d_o"], cfg["n"]
     bits, group, B, iters = cfg["bits"], cfg["group"], cfg["B"], cfg["iters"]
     seed = cfg.get("seed", 1)
@@ -178,7 +185,7 @@ def main():
             record.append((e, out["residuals"]))
         return gp, ap
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step(None)
     torch.cuda.synchronize()
 
@@ -187,7 +194,7 @@ def main():
     recs = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         step(recs)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -201,11 +208,9 @@ def main():
         for k, v in zip(ph, vals):
             ph[k].append(v)
     med = {k: float(np.median(v)) for k, v in ph.items()}
-    admm_loop_ms = 0.0
-    # the ADMM call's loop = its kernels minus the one-time set-up product
     kn = {k: v for k, v in kt.items()}
     loop_kinds = ("gemm_admm_wupdate1", "gemm_admm_wupdate2", "admm_project")
-    admm_loop_ms = sum(kn[k][1] for k in loop_kinds if k in kn) / args.steps
+    admm_loop_ms = sum(kn[k][1] for k in loop_kinds if k in kn) / steps
     admm_call_ms = med["admm"]
     iters_per_s = iters / (admm_call_ms / 1e3)
     iters_per_s_loop = iters / (admm_loop_ms / 1e3) if admm_loop_ms > 0 else None
@@ -220,14 +225,23 @@ def main():
     hb_flops = 1.0 * n * d_i * (d_i + 1)                    # upper triangle of X^T X
     gemm1_bytes = 4.0 * (2 * d_o * d_i + d_i * d_i + d_o * d_i)   # read M, P, V; write T
     gemm2_bytes = 4.0 * (d_o * d_i + d_i * d_i + d_o * d_i)       # read T, V; write W~
-    alg_bytes = {"gemm_admm_wupdate1": gemm1_bytes, "gemm_admm_wupdate2": gemm2_bytes,
-                 "admm_project": proj_bytes, "hessian_gram_bf16": 2.0 * n * d_i}
+    tr_flops, ib_flops = gptq_work(d_o, d_i, B)
+    n_blocks = -(-d_i // B)
+    pack_bytes = d_o * d_i * (1.0 + bits / 8.0)
+    # per launch: the trailing product and the block kernel run once per block (the
+    # last block has no trailing product); the R factor and packing once per layer
+    rows = (
+        ("gemm_admm_wupdate1", gemm_flops, PEAK_FP32_MFMA, "mfma", "TFLOP/s", gemm1_bytes),
+        ("gemm_admm_wupdate2", gemm_flops, PEAK_FP32_MFMA, "mfma", "TFLOP/s", gemm2_bytes),
+        ("admm_project", proj_bytes, PEAK_HBM, "hbm", "GB/s", proj_bytes),
+        ("hessian_gram_bf16", hb_flops, PEAK_BF16, "mfma", "TFLOP/s", 2.0 * n * d_i),
+        ("gemm_gptq_trailing", tr_flops / max(n_blocks - 1, 1), PEAK_FP32_MFMA, "mfma", "TFLOP/s", None),
+        ("gptq_block", ib_flops / n_blocks, PEAK_FP32_VALU, "alu", "TFLOP/s", None),
+        ("rfactor_fp64", 2.0 / 3.0 * d_i ** 3, PEAK_FP64, "alu", "TFLOP/s", None),
+        ("pack", pack_bytes, PEAK_HBM, "hbm", "GB/s", pack_bytes),
+    )
     rl = []
-    for kind, work, peak, bound, unit in (
-            ("gemm_admm_wupdate1", gemm_flops, PEAK_FP32_MFMA, "mfma", "TFLOP/s"),
-            ("gemm_admm_wupdate2", gemm_flops, PEAK_FP32_MFMA, "mfma", "TFLOP/s"),
-            ("admm_project", proj_bytes, PEAK_HBM, "hbm", "GB/s"),
-            ("hessian_gram_bf16", hb_flops, PEAK_BF16, "mfma", "TFLOP/s")):
+    for kind, work, peak, bound, unit, alg in rows:
         a = avg_ms(kind)
         if a is None:
             continue
@@ -236,8 +250,8 @@ def main():
         rl.append({"kernel": kind, "bound": bound, "achieved": round(rate / scale, 3),
                    "peak": round(peak / scale, 3), "unit": unit, "frac": round(rate / peak, 4),
                    "avg_ms": round(a, 4), "launches": kn[kind][0],
-                   "traffic": traffic_bytes(kind, args.workload),
-                   "traffic_unit": "B/launch", "algorithmic_bytes": alg_bytes[kind]})
+                   "traffic": traffic_bytes(kind, name),
+                   "traffic_unit": "B/launch", "algorithmic_bytes": alg})
     dominant = max((r for r in rl if r["kernel"].startswith("gemm_admm")),
                    key=lambda r: r["avg_ms"] * r["launches"], default=None)
 
@@ -248,15 +262,15 @@ def main():
         "value": round(iters_per_s, 3),
         "unit": "iters/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 3),
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(wall / steps * 1e3, 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": args.workload, "d_i": d_i, "d_o": d_o, "bits": bits, "group": group,
+        "config": {"workload": name, "d_i": d_i, "d_o": d_o, "bits": bits, "group": group,
                    "n_tokens": n, "gptq_block": B, "admm_iters": iters, "rho0": cfg["rho0"],
                    "gamma": cfg["gamma"], "refresh_every": cfg["refresh"],
                    "global_batch": n, "parallelism": "single-gpu"},
@@ -281,10 +295,37 @@ def main():
                                                     "traffic", "traffic_unit", "algorithmic_bytes",
                                                     "kernel")},
     }
-    if not args.no_cpu:
+    if with_cpu:
         Xh = X[:16384].view(torch.int16).cpu().numpy().view(np.uint16)
         Wh = W[:args.cpu_rows].view(torch.int16).cpu().numpy().view(np.uint16)
         line["cpu_baseline"] = cpu_baseline(cfg, Xh, Wh, args.cpu_rows, args.cpu_iters)
+    del X, W, H, ws_h, ws_g, ws_a
+    torch.cuda.empty_cache()
+    return line
+
+
+SWEEP = ("attn_4096x4096_w3g128", "up_4096x12288_w3g128", "mlp_up_4096x12288_w2g128",
+         "mlp_down_12288x4096_w2g128", "32b_up_5120x25600_w3g128", "32b_down_25600x5120_w3g128")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the quantizer's rows shard "
+              f"across GPUs without per-iteration exchange, but no multi-GPU path is built.",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
+    if args.sweep:
+        # one line per layer workload (the tiny layer excluded), one timed step each
+        for name in SWEEP:
+            line = run_workload(args, name, 1, 1, False)
+            line["sweep"] = True
+            print(json.dumps(line), flush=True)
+        return
+    line = run_workload(args, args.workload, args.steps, args.warmup, not args.no_cpu)
     print(json.dumps(line), flush=True)
 
 

@@ -72,7 +72,7 @@ size_t admm_ws(int64_t d_o, int64_t d_i, int64_t group, int64_t iters) {
   c.take<float>(static_cast<size_t>(d_o) * G);           // s_0 scratch
   c.take<uint8_t>(static_cast<size_t>(d_o) * G);         // z_0 scratch
   c.take<float>(static_cast<size_t>(d_i));               // 1 / sigma
-  c.take<double>(static_cast<size_t>(iters > 0 ? iters : 1) * admm_proj_blocks(G) * 2);
+  c.take<double>(static_cast<size_t>(iters > 0 ? iters : 1) * admm_proj_blocks(G, d_o) * 2);
   return c.used;
 }
 
@@ -275,7 +275,7 @@ int qz_admmq(const float* V, const float* Lambda, const float* sigma, const void
   const int group = grid->group_size, bits = grid->bits;
   const int64_t ld = round_up(d_i, 4);
   const int64_t G = d_i / group;
-  const int nblk = admm_proj_blocks(d_i / grid->group_size);
+  const int nblk = admm_proj_blocks(d_i / grid->group_size, d_o);
   Carver cv(ws);
   uint32_t* flag = cv.take<uint32_t>(1);
   float* Vt = cv.take<float>(static_cast<size_t>(d_i) * ld);

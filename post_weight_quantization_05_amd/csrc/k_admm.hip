@@ -27,12 +27,15 @@ namespace qz {
 namespace {
 
 constexpr int kThreads = 256;
-// Wavefronts of the projection launch: about 131072 (32768 workgroups, many bytes in
-// flight), rounded to a multiple of the number of groups per row so that every
-// wavefront keeps one column group and strides over rows.
+// Wavefronts of the projection launch: one per three (row, group) pairs, at most
+// 131072 (32768 workgroups: many bytes in flight, a few rows per wavefront to spread
+// its start-up), rounded down to a multiple of the number of groups per row so that
+// every wavefront keeps one column group and strides over rows.
 constexpr int64_t kProjWaves = 131072;
-__host__ __device__ inline int64_t proj_waves(int64_t G) {
-  const int64_t per = kProjWaves / G;
+__host__ __device__ inline int64_t proj_waves(int64_t G, int64_t d_o) {
+  int64_t target = d_o * G / 3;
+  if (target > kProjWaves) target = kProjWaves;
+  const int64_t per = target / G;
   return (per > 0 ? per : 1) * G;
 }
 
@@ -201,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void project_reg_kernel(const AdmmProj p,
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
   const int64_t G = p.d_i / p.group;
-  const int64_t nwaves = proj_waves(G);
+  const int64_t nwaves = proj_waves(G, p.d_o);
   const int64_t w = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + wid;
   const float maxq = static_cast<float>((1 << p.bits) - 1);
   const float rs = p.rescale ? p.rho / p.rho_next : 1.0f;
@@ -395,7 +398,9 @@ inline unsigned grid_for(int64_t n) {
 
 }  // namespace
 
-int admm_proj_blocks(int64_t G) { return static_cast<int>(ceil_div(proj_waves(G > 0 ? G : 1), int64_t{kThreads / 64})); }
+int admm_proj_blocks(int64_t G, int64_t d_o) {
+  return static_cast<int>(ceil_div(proj_waves(G > 0 ? G : 1, d_o > 0 ? d_o : 1), int64_t{kThreads / 64}));
+}
 
 int launch_admm_project(const AdmmProj& p, hipStream_t s, const float* inv_sigma) {
   // register-resident path when a group is exactly 64, 128 or 256 columns and every row
@@ -403,7 +408,7 @@ int launch_admm_project(const AdmmProj& p, hipStream_t s, const float* inv_sigma
   const bool al = (p.d_i % 4 == 0) && (p.ldw % 4 == 0) && (p.ldm % 4 == 0) &&
                   (reinterpret_cast<uintptr_t>(p.U) % 16 == 0) &&
                   (reinterpret_cast<uintptr_t>(p.codes) % 4 == 0);
-  const int nb = admm_proj_blocks(p.d_i / p.group);
+  const int nb = admm_proj_blocks(p.d_i / p.group, p.d_o);
   if (al && p.group == 128)
     project_reg_kernel<2><<<nb, kThreads, 0, s>>>(p, inv_sigma);
   else if (al && p.group == 256)

@@ -183,7 +183,7 @@ struct AdmmProj {
   int rescale;                       // 1: U *= rho/rho_next
   double* partial;                   // [nblocks x 2] for this iteration
 };
-int admm_proj_blocks(int64_t G);   // workgroups of a projection launch (partials per iteration)
+int admm_proj_blocks(int64_t G, int64_t d_o);   // workgroups of a projection launch (partials per iteration)
 int launch_admm_project(const AdmmProj& p, hipStream_t s, const float* inv_sigma);
 int launch_admm_init_m(const uint8_t* codes, const float* scales, const uint8_t* zeros,
                        const float* U, const float* sigma, int64_t d_o, int64_t d_i, int group,
