@@ -295,6 +295,18 @@ def run_workload(args, name, steps, warmup, with_cpu):
                                                     "traffic", "traffic_unit", "algorithmic_bytes",
                                                     "kernel")},
     }
+    # layer objective of both results on the full-token H (outside the timed steps)
+    gc, gs, gz = q.qz_gptq(H, W, bits, group, B, ws=ws_g)
+    f_gptq = q.qz_objective(H, W, gc, gs, gz, group)
+    V, lam, sig = q.qz_admmq_prepare(H)
+    ao = q.qz_admmq(V, lam, sig, W, bits, group, iters, cfg["rho0"], cfg["gamma"], cfg["refresh"],
+                    ws=ws_a, want_U=False)
+    f_admm = q.qz_objective(H, W, ao["codes"], ao["scales"], ao["zeros"], group)
+    cr, cs, cz = q.qz_rtn(W, bits, group)
+    f_rtn = q.qz_objective(H, W, cr, cs, cz, group)
+    del V, lam, sig, ao
+    line["components"]["objective"] = {"rtn": f_rtn, "gptq": f_gptq, "admmq": f_admm,
+                                       "admmq_over_gptq": round(f_admm / f_gptq, 4)}
     if with_cpu:
         Xh = X[:16384].view(torch.int16).cpu().numpy().view(np.uint16)
         Wh = W[:args.cpu_rows].view(torch.int16).cpu().numpy().view(np.uint16)

@@ -213,6 +213,25 @@ int qz_pack(const uint8_t* codes, int64_t rows, int64_t cols, int32_t bits, uint
 int qz_unpack(const uint32_t* in, int64_t rows, int64_t cols, int32_t bits, uint8_t* codes,
               hipStream_t stream);
 
+/* -------------------------------------------------------------- objective --
+ * The layer objective both solvers minimise (ADMM-Q summary, methodology, 1.
+ * problem formulation; GPTQ tutorial, section 2, the curvature-weighted cost):
+ *   f = 1/2 sum_r (q_r - w_r)^T H (q_r - w_r),   q = s (C - z) per (row, group),
+ * with w_r the rows of W_hat.  Computed as D = Q - W_hat (fp32), the product D H
+ * on the matrix cores with each output element multiplied by D in the same pass
+ * (D H is never stored), row sums in fp64 in a fixed order.
+ *   H [d_i x d_i] fp32 symmetric; W_hat [d_o x d_i] (dtype wt); codes [d_o x d_i];
+ *   scales, zeros [d_o x d_i/group_size].
+ *   row_f (device, nullable): [d_o] fp64 per-row objectives.
+ *   out_host (host, nullable): f.  When given the call is SYNC and reports a
+ *   non-finite weight or scale as QZ_ENONFINITE; otherwise it is asynchronous.
+ *   ws: qz_objective_workspace(d_o, d_i) bytes, 256-byte aligned.            */
+size_t qz_objective_workspace(int64_t d_o, int64_t d_i);
+int qz_objective(const float* H, const void* W_hat, int32_t wt, const uint8_t* codes,
+                 const float* scales, const uint8_t* zeros, int64_t d_o, int64_t d_i,
+                 int32_t group_size, double* row_f, double* out_host, void* ws,
+                 size_t ws_bytes, hipStream_t stream);
+
 /* ----------------------------------------------------------------- timing --
  * Per-kernel timing for measurement tools: while enabled, the library records a
  * HIP event pair around each of its kernel launches, on the stream the kernel

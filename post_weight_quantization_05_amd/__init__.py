@@ -194,6 +194,27 @@ def qz_admmq(V, Lambda, sigma, W_hat, bits, group, iters, rho0, gamma, refresh_e
     return dict(codes=codes, scales=scales, zeros=zeros, U=U, residuals=res[:iters])
 
 
+def qz_objective_workspace(d_o, d_i) -> int:
+    return lib().qz_objective_workspace(d_o, d_i)
+
+
+def qz_objective(H, W_hat, codes, scales, zeros, group, rows=False, ws=None):
+    """f = 1/2 sum_r (q_r - w_r)^T H (q_r - w_r) for q = s (codes - z).  Returns the float
+    (and, with rows=True, the per-row fp64 objectives as a device tensor)."""
+    torch = _torch()
+    for t, nm in ((H, "H"), (W_hat, "W_hat"), (codes, "codes"), (scales, "scales"), (zeros, "zeros")):
+        _dev(t, nm)
+    d_o, d_i = W_hat.shape
+    if ws is None:
+        ws = _workspace(lib().qz_objective_workspace(d_o, d_i), W_hat.device)
+    row_f = torch.empty(d_o, dtype=torch.float64, device=W_hat.device) if rows else None
+    out = C.c_double(0.0)
+    _check(lib().qz_objective(_ptr(H), _ptr(W_hat), _dtype_code(W_hat), _ptr(codes), _ptr(scales),
+                              _ptr(zeros), d_o, d_i, int(group), _ptr(row_f), C.byref(out),
+                              _ptr(ws), ws.numel(), _stream()))
+    return (out.value, row_f) if rows else out.value
+
+
 def qz_packed_words(cols, bits) -> int:
     return lib().qz_packed_words(cols, bits)
 

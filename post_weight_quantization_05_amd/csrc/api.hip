@@ -48,6 +48,15 @@ int check_grid(const qz_grid* g, int64_t d_i) {
   return QZ_OK;
 }
 
+size_t objective_ws(int64_t d_o, int64_t d_i) {
+  Carver c(nullptr);
+  c.take<uint32_t>(1);
+  c.take<float>(static_cast<size_t>(d_o) * round_up(d_i, 4));          // D = Q - W_hat
+  c.take<double>(static_cast<size_t>(d_o) * gemm_tile_cols(d_i));      // row partials
+  c.take<double>(1);                                                    // total
+  return c.used;
+}
+
 size_t gptq_ws(int64_t d_o, int64_t d_i) {
   Carver c(nullptr);
   c.take<uint32_t>(1);
@@ -397,6 +406,61 @@ int qz_unpack(const uint32_t* in, int64_t rows, int64_t cols, int32_t bits, uint
   set_error("");
   ScopedTimer tm(K_PACK, stream);
   return launch_unpack(in, rows, cols, bits, codes, stream);
+}
+
+// ------------------------------------------------------------------ objective
+size_t qz_objective_workspace(int64_t d_o, int64_t d_i) {
+  if (d_o < 0 || d_i < 1) return 0;
+  return objective_ws(d_o, d_i);
+}
+
+int qz_objective(const float* H, const void* W_hat, int32_t wt, const uint8_t* codes,
+                 const float* scales, const uint8_t* zeros, int64_t d_o, int64_t d_i,
+                 int32_t group_size, double* row_f, double* out_host, void* ws, size_t ws_bytes,
+                 hipStream_t stream) {
+  if (!valid_dtype(wt)) return fail(QZ_EINVAL, "objective: bad dtype");
+  if (d_o < 0 || d_i < 1) return fail(QZ_EINVAL, "objective: need d_o >= 0 and d_i >= 1");
+  if (group_size < 1 || d_i % group_size != 0)
+    return fail(QZ_EINVAL, "objective: group_size must divide d_i");
+  if (!H || (d_o > 0 && (!W_hat || !codes || !scales || !zeros)))
+    return fail(QZ_EINVAL, "objective: null pointer");
+  const size_t need = objective_ws(d_o, d_i);
+  if (ws_bytes < need || !ws) return fail(QZ_EWORKSPACE, "objective: workspace too small");
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0)
+    return fail(QZ_EWORKSPACE, "objective: workspace must be 256-byte aligned");
+  set_error("");
+  if (d_o == 0) {
+    if (out_host) *out_host = 0.0;
+    return QZ_OK;
+  }
+  const int64_t ld = round_up(d_i, 4);
+  const int tcols = gemm_tile_cols(d_i);
+  Carver cv(ws);
+  uint32_t* flag = cv.take<uint32_t>(1);
+  float* D = cv.take<float>(static_cast<size_t>(d_o) * ld);
+  double* dpart = cv.take<double>(static_cast<size_t>(d_o) * tcols);
+  double* total = cv.take<double>(1);
+  {
+    ScopedTimer tm(K_OBJECTIVE, stream);
+    QZ_TRY(launch_fill_u32(flag, 1, 0u, stream));
+    QZ_TRY(launch_dequant_diff(codes, scales, zeros, W_hat, wt, d_o, d_i, group_size, D, ld, flag,
+                               stream));
+    GemmArgs g{};
+    g.M = d_o; g.N = d_i; g.K = d_i;
+    g.A = D; g.lda = ld;
+    g.B = H; g.ldb = d_i;          // H symmetric: row n of H is column n
+    g.dpart = dpart;
+    QZ_TRY(launch_gemm_nt(EPI_DOTROW, g, stream));
+    QZ_TRY(launch_rowsum_half(dpart, d_o, tcols, row_f, total, stream));
+  }
+  if (out_host) {
+    if (hipMemcpyAsync(out_host, total, sizeof(double), hipMemcpyDeviceToHost, stream) != hipSuccess)
+      return fail(QZ_EHIP, "objective: copy of the result failed");
+    uint32_t h = 0;
+    QZ_TRY(read_flag(flag, stream, &h));   // synchronises the stream
+    if (h & FLAG_NONFINITE) return fail(QZ_ENONFINITE, "objective: non-finite weight or grid");
+  }
+  return QZ_OK;
 }
 
 }  // extern "C"

@@ -152,6 +152,35 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_nt_kernel(const GemmArgs g) 
 
   // Epilogue.  32x32 accumulator layout: register r of lane l holds
   // row 8*(r/4) + 4*(l/32) + r%4, column l%32 of the block.
+  if constexpr (EPI == EPI_DOTROW) {
+    // per row: sum over this tile's columns of acc * A[row][col] in fp64, reduced across
+    // the 32 lanes of a half-wave (xor pattern) and then across the two column waves in
+    // LDS, both in a fixed order
+    __syncthreads();   // the operand buffer becomes the row-sum scratch
+    double* red = reinterpret_cast<double*>(As);   // [2][BM]
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rl = wm * 64 + mt * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int64_t row = m0 + rl;
+        double v = 0.0;
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const int64_t col = n0 + wn * 64 + nt * 32 + (lane & 31);
+          if (row < g.M && col < g.N)
+            v += static_cast<double>(acc[mt][nt][r]) * static_cast<double>(g.A[row * g.lda + col]);
+        }
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1) v += __shfl_xor(v, off);
+        if ((lane & 31) == 0) red[wn * BM + rl] = v;
+      }
+    }
+    __syncthreads();
+    if (tid < BM && m0 + tid < g.M)
+      g.dpart[(m0 + tid) * tn_n + tn] = red[tid] + red[BM + tid];
+    return;
+  }
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const int64_t col = n0 + wn * 64 + nt * 32 + (lane & 31);
@@ -193,6 +222,8 @@ int launch_epi(const GemmArgs& a, hipStream_t s) {
 
 }  // namespace
 
+int gemm_tile_cols(int64_t N) { return static_cast<int>(ceil_div(N, int64_t{BN})); }
+
 int launch_gemm_nt(int epi, const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return QZ_OK;
   switch (epi) {
@@ -201,6 +232,9 @@ int launch_gemm_nt(int epi, const GemmArgs& a, hipStream_t s) {
     case EPI_COLSCALE: return launch_epi<EPI_COLSCALE>(a, s);
     case EPI_ADMM1: return launch_epi<EPI_ADMM1>(a, s);
     case EPI_ADD: return launch_epi<EPI_ADD>(a, s);
+    case EPI_DOTROW:
+      if (a.N != a.K || !a.dpart) return fail(QZ_EINVAL, "gemm: row-dot epilogue needs N == K");
+      return launch_epi<EPI_DOTROW>(a, s);
   }
   return fail(QZ_EINVAL, "gemm: bad epilogue");
 }

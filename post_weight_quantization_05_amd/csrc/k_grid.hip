@@ -208,6 +208,51 @@ __global__ __launch_bounds__(kThreads) void zero_u32_kernel(uint32_t* __restrict
     p[j] = 0u;
 }
 
+// D = s (C - z) - W_hat per element (the dequantized weights' error), fp32.
+template <int WT>
+__global__ __launch_bounds__(kThreads) void dequant_diff_kernel(
+    const uint8_t* __restrict__ codes, const float* __restrict__ scales,
+    const uint8_t* __restrict__ zeros, const void* __restrict__ W, int64_t rows, int64_t cols,
+    int group, float* __restrict__ out, int64_t ldo, uint32_t* __restrict__ flag) {
+  const int64_t total = rows * cols;
+  const int64_t G = cols / group;
+  bool bad = false;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = e / cols, j = e % cols;
+    const int64_t gi = r * G + j / group;
+    const float q = scales[gi] * (static_cast<float>(codes[e]) - static_cast<float>(zeros[gi]));
+    const float v = q - load_w<WT>(W, e);
+    bad |= !__builtin_isfinite(v);
+    out[r * ldo + j] = v;
+  }
+  if (flag && __any(bad) && (threadIdx.x & 63) == 0) atomicOr(flag, FLAG_NONFINITE);
+}
+
+// row_f[r] = sum_t dpart[r][t] / 2 in order; total = sum_r row_f[r]: per-thread strided
+// sums, then a tree in LDS (fixed order).
+__global__ __launch_bounds__(kThreads) void rowsum_half_kernel(const double* __restrict__ dpart,
+                                                               int64_t rows, int64_t tcols,
+                                                               double* __restrict__ row_f,
+                                                               double* __restrict__ total) {
+  __shared__ double red[kThreads];
+  double acc = 0.0;
+  for (int64_t r = threadIdx.x; r < rows; r += kThreads) {
+    double v = 0.0;
+    for (int64_t t = 0; t < tcols; ++t) v += dpart[r * tcols + t];
+    v *= 0.5;
+    if (row_f) row_f[r] = v;
+    acc += v;
+  }
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int h = kThreads / 2; h > 0; h >>= 1) {
+    if (threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *total = red[0];
+}
+
 }  // namespace
 
 int launch_check_perm(const int32_t* perm, int64_t d, uint32_t* counts, uint32_t* flag,
@@ -282,6 +327,27 @@ int launch_to_f32(const void* W, int wt, int64_t rows, int64_t cols, const int32
   else
     to_f32_kernel<QZ_F32><<<nb, kThreads, 0, s>>>(W, rows, cols, perm, div, out, ldo, flag);
   return check_launch("to_f32");
+}
+
+int launch_dequant_diff(const uint8_t* codes, const float* scales, const uint8_t* zeros,
+                        const void* W, int wt, int64_t rows, int64_t cols, int group, float* out,
+                        int64_t ldo, uint32_t* flag, hipStream_t s) {
+  const int64_t n = rows * cols;
+  if (n == 0) return QZ_OK;
+  const int nb = blocks_for(n, kThreads * 4, 65536);
+  if (wt == QZ_BF16)
+    dequant_diff_kernel<QZ_BF16><<<nb, kThreads, 0, s>>>(codes, scales, zeros, W, rows, cols, group,
+                                                          out, ldo, flag);
+  else
+    dequant_diff_kernel<QZ_F32><<<nb, kThreads, 0, s>>>(codes, scales, zeros, W, rows, cols, group,
+                                                         out, ldo, flag);
+  return check_launch("dequant_diff");
+}
+
+int launch_rowsum_half(const double* dpart, int64_t rows, int64_t tcols, double* row_f,
+                       double* total, hipStream_t s) {
+  rowsum_half_kernel<<<1, kThreads, 0, s>>>(dpart, rows, tcols, row_f, total);
+  return check_launch("rowsum");
 }
 
 int launch_check_finite_f32(const float* p, int64_t n, uint32_t* flag, hipStream_t s) {

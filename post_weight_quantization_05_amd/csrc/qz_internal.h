@@ -54,6 +54,7 @@ enum KernelKind : int {
   K_GRID_RTN,
   K_PACK,
   K_EIG,
+  K_OBJECTIVE,
   K_KIND_COUNT
 };
 // Records an event pair around the enclosed launches when timing is enabled.
@@ -127,6 +128,14 @@ int launch_unpack(const uint32_t* in, int64_t rows, int64_t cols, int bits, uint
 int launch_to_f32(const void* W, int wt, int64_t rows, int64_t cols, const int32_t* perm,
                   const float* div, float* out, int64_t ldo, uint32_t* flag, hipStream_t s);
 int launch_check_finite_f32(const float* p, int64_t n, uint32_t* flag, hipStream_t s);
+// D = s (C - z) - W_hat  (fp32 [rows x ldo], zero padding columns up to ldo); sets
+// FLAG_NONFINITE on a non-finite value
+int launch_dequant_diff(const uint8_t* codes, const float* scales, const uint8_t* zeros,
+                        const void* W, int wt, int64_t rows, int64_t cols, int group, float* out,
+                        int64_t ldo, uint32_t* flag, hipStream_t s);
+// row_f[r] = 0.5 * sum_t dpart[r][t]; total = sum_r row_f[r] (fixed order, one workgroup)
+int launch_rowsum_half(const double* dpart, int64_t rows, int64_t tcols, double* row_f,
+                       double* total, hipStream_t s);
 // Sets FLAG_BADARG unless perm[0..d) is a permutation of 0..d-1 (counts: d ints of scratch).
 int launch_check_perm(const int32_t* perm, int64_t d, uint32_t* counts, uint32_t* flag, hipStream_t s);
 
@@ -137,6 +146,8 @@ enum GemmEpi : int {
   EPI_COLSCALE = 2,  // C = acc * colv[n]
   EPI_ADMM1 = 3,     // C = (P + rho * acc) / (colv[n] + rho)
   EPI_ADD = 4,       // C = C + acc
+  EPI_DOTROW = 5,    // dpart[m][tile column] = sum over the tile's columns of acc * A[m][n]
+                     // (C unused; needs N == K so that A[m][n] exists)
 };
 struct GemmArgs {
   int64_t M, N, K;
@@ -146,7 +157,9 @@ struct GemmArgs {
   const float* P; int64_t ldp;   // EPI_ADMM1
   const float* colv;             // EPI_COLSCALE / EPI_ADMM1
   float rho;
+  double* dpart;                 // EPI_DOTROW: [M x ceil(N / 128)]
 };
+int gemm_tile_cols(int64_t N);   // ceil(N / 128): tile columns of the GEMM
 int launch_gemm_nt(int epi, const GemmArgs& a, hipStream_t s);
 
 // bf16 Hessian (k_hessian.hip)
