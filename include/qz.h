@@ -232,6 +232,30 @@ int qz_objective(const float* H, const void* W_hat, int32_t wt, const uint8_t* c
                  int32_t group_size, double* row_f, double* out_host, void* ws,
                  size_t ws_bytes, hipStream_t stream);
 
+/* ----------------------------------------------------------- local search --
+ * Pairwise-swap local search after a solver (ADMM-Q summary, methodology, 2. key
+ * algorithmic components, the local-search item: discrete moves that swap values
+ * between positions of an output channel, evaluated by their direct effect on the
+ * reconstruction error, in parallel).  The grid (scales, zeros) stays fixed.  Moves
+ * are defined inside one group: one code +-1, or two codes j < k changed by a, b in
+ * {-1, +1}.  Each step: the gradient (Q - W_hat) H on the matrix cores; every
+ * (row, group) proposes its move with the smallest exact change of the objective
+ * (qz_objective's f) if negative, ties to the smallest (j, k, a, b); each row accepts
+ * proposals in ascending group order while the change plus the exact interaction with
+ * the moves it already accepted stays negative, then applies them, so f never rises.
+ *   grid: bits and group_size (at most 128 columns; it divides d_i); scales, zeros
+ *   [d_o x d_i/group_size] are inputs.  codes [d_o x d_i] u8 in/out.
+ *   max_steps >= 0; the search stops after a step that accepts no move.
+ *   moves_host (host, nullable): [max_steps] moves accepted per step (entries past
+ *   the last step run are not written); steps_host (host, nullable): steps that
+ *   accepted at least one move.  SYNC (every step reads the move count).
+ *   ws: qz_local_search_workspace(d_o, d_i, group_size) bytes, 256-byte aligned.  */
+size_t qz_local_search_workspace(int64_t d_o, int64_t d_i, int32_t group_size);
+int qz_local_search(const float* H, const void* W_hat, int32_t wt, int64_t d_o, int64_t d_i,
+                    const qz_grid* grid, const float* scales, const uint8_t* zeros,
+                    uint8_t* codes, int32_t max_steps, int32_t* moves_host,
+                    int32_t* steps_host, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* ----------------------------------------------------------------- timing --
  * Per-kernel timing for measurement tools: while enabled, the library records a
  * HIP event pair around each of its kernel launches, on the stream the kernel

@@ -148,7 +148,7 @@ def step_row(H, w, codes, scale, zero, bits, group, hint=None, tol=0.0):
                             for g2, m, _ in accepted)
         take = run < 0
         if hint is not None:
-            hinted = theirs is not None and prop is theirs
+            hinted = theirs is not None and tuple(prop[1:]) == tuple(theirs[1:])
             if take != hinted and abs(run) <= tol:
                 take = hinted
                 adopted += 1

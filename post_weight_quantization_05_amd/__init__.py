@@ -215,6 +215,27 @@ def qz_objective(H, W_hat, codes, scales, zeros, group, rows=False, ws=None):
     return (out.value, row_f) if rows else out.value
 
 
+def qz_local_search_workspace(d_o, d_i, group) -> int:
+    return lib().qz_local_search_workspace(d_o, d_i, group)
+
+
+def qz_local_search(H, W_hat, codes, scales, zeros, bits, group, max_steps, ws=None):
+    """Pairwise-swap local search on the fixed grid; codes are updated in place.
+    Returns (steps that moved, [moves accepted per step])."""
+    for t, nm in ((H, "H"), (W_hat, "W_hat"), (codes, "codes"), (scales, "scales"), (zeros, "zeros")):
+        _dev(t, nm)
+    d_o, d_i = W_hat.shape
+    if ws is None:
+        ws = _workspace(lib().qz_local_search_workspace(d_o, d_i, group), W_hat.device)
+    moves = (C.c_int32 * max(int(max_steps), 1))()
+    steps = C.c_int32(0)
+    g = _grid(bits, group, True)
+    _check(lib().qz_local_search(_ptr(H), _ptr(W_hat), _dtype_code(W_hat), d_o, d_i, C.byref(g),
+                                 _ptr(scales), _ptr(zeros), _ptr(codes), int(max_steps), moves,
+                                 C.byref(steps), _ptr(ws), ws.numel(), _stream()))
+    return steps.value, list(moves)[:steps.value + (1 if steps.value < max_steps else 0)]
+
+
 def qz_packed_words(cols, bits) -> int:
     return lib().qz_packed_words(cols, bits)
 

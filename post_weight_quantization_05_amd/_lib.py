@@ -24,7 +24,8 @@ STATUS_NAMES = {0: "QZ_OK", -1: "QZ_EINVAL", -2: "QZ_ENOTPD", -3: "QZ_ENONFINITE
 # every entry point declared in include/qz.h
 EXPORTS = ("qz_hessian_workspace", "qz_build_hessian", "qz_rtn", "qz_gptq_workspace", "qz_gptq",
            "qz_admmq_prepare", "qz_admmq_workspace", "qz_admmq", "qz_objective_workspace",
-           "qz_objective", "qz_packed_words", "qz_pack",
+           "qz_objective", "qz_local_search_workspace", "qz_local_search", "qz_packed_words",
+           "qz_pack",
            "qz_unpack", "qz_timing_enable", "qz_timing_read", "qz_timing_kind_name",
            "qz_last_error", "qz_abi_version")
 
@@ -59,6 +60,9 @@ _SIGS = {
                            P, P, P, SZ, P]),
     "qz_objective_workspace": (SZ, [I64, I64]),
     "qz_objective": (C.c_int, [P, P, I32, P, P, P, I64, I64, I32, P, P, P, SZ, P]),
+    "qz_local_search_workspace": (SZ, [I64, I64, I32]),
+    "qz_local_search": (C.c_int, [P, P, I32, I64, I64, C.POINTER(QzGrid), P, P, P, I32, P, P, P,
+                                  SZ, P]),
     "qz_packed_words": (I64, [I64, I32]),
     "qz_pack": (C.c_int, [P, I64, I64, I32, P, P]),
     "qz_unpack": (C.c_int, [P, I64, I64, I32, P, P]),

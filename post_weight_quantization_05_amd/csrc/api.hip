@@ -57,6 +57,18 @@ size_t objective_ws(int64_t d_o, int64_t d_i) {
   return c.used;
 }
 
+size_t lsearch_ws(int64_t d_o, int64_t d_i, int64_t group) {
+  const int64_t G = d_i / group;
+  Carver c(nullptr);
+  c.take<uint32_t>(1);
+  c.take<float>(static_cast<size_t>(d_o) * round_up(d_i, 4));   // D = Q - W_hat
+  c.take<float>(static_cast<size_t>(d_o) * round_up(d_i, 4));   // gradient D H
+  c.take<float>(static_cast<size_t>(d_o) * G);                   // proposal change
+  c.take<int32_t>(static_cast<size_t>(d_o) * G);                 // proposal index
+  c.take<int32_t>(1);                                             // accepted moves
+  return c.used;
+}
+
 size_t gptq_ws(int64_t d_o, int64_t d_i) {
   Carver c(nullptr);
   c.take<uint32_t>(1);
@@ -460,6 +472,75 @@ int qz_objective(const float* H, const void* W_hat, int32_t wt, const uint8_t* c
     QZ_TRY(read_flag(flag, stream, &h));   // synchronises the stream
     if (h & FLAG_NONFINITE) return fail(QZ_ENONFINITE, "objective: non-finite weight or grid");
   }
+  return QZ_OK;
+}
+
+// ------------------------------------------------------------------ local search
+size_t qz_local_search_workspace(int64_t d_o, int64_t d_i, int32_t group_size) {
+  if (d_o < 0 || d_i < 1 || group_size < 1 || d_i % group_size != 0) return 0;
+  return lsearch_ws(d_o, d_i, group_size);
+}
+
+int qz_local_search(const float* H, const void* W_hat, int32_t wt, int64_t d_o, int64_t d_i,
+                    const qz_grid* grid, const float* scales, const uint8_t* zeros,
+                    uint8_t* codes, int32_t max_steps, int32_t* moves_host, int32_t* steps_host,
+                    void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!valid_dtype(wt)) return fail(QZ_EINVAL, "local_search: bad dtype");
+  if (d_o < 0 || d_i < 1) return fail(QZ_EINVAL, "local_search: need d_o >= 0 and d_i >= 1");
+  QZ_TRY(check_grid(grid, d_i));
+  const int group = grid->group_size, bits = grid->bits;
+  if (group > ls_max_group())
+    return fail(QZ_EINVAL, "local_search: groups of at most 128 columns are supported");
+  if (max_steps < 0) return fail(QZ_EINVAL, "local_search: max_steps must be >= 0");
+  const int64_t G = d_i / group;
+  if (ls_accept_lds(G) > 65536) return fail(QZ_EINVAL, "local_search: too many groups per row");
+  if (!H || (d_o > 0 && (!W_hat || !codes || !scales || !zeros)))
+    return fail(QZ_EINVAL, "local_search: null pointer");
+  const size_t need = lsearch_ws(d_o, d_i, group);
+  if (ws_bytes < need || !ws) return fail(QZ_EWORKSPACE, "local_search: workspace too small");
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0)
+    return fail(QZ_EWORKSPACE, "local_search: workspace must be 256-byte aligned");
+  set_error("");
+  if (steps_host) *steps_host = 0;
+  if (d_o == 0 || max_steps == 0) return QZ_OK;
+  const int64_t ld = round_up(d_i, 4);
+  Carver cv(ws);
+  uint32_t* flag = cv.take<uint32_t>(1);
+  float* D = cv.take<float>(static_cast<size_t>(d_o) * ld);
+  float* Gm = cv.take<float>(static_cast<size_t>(d_o) * ld);
+  float* best_df = cv.take<float>(static_cast<size_t>(d_o) * G);
+  int32_t* best_idx = cv.take<int32_t>(static_cast<size_t>(d_o) * G);
+  int32_t* counter = cv.take<int32_t>(1);
+  QZ_TRY(launch_fill_u32(flag, 1, 0u, stream));
+  int steps = 0;
+  for (int t = 0; t < max_steps; ++t) {
+    {
+      ScopedTimer tm(K_LSEARCH, stream);
+      QZ_TRY(launch_dequant_diff(codes, scales, zeros, W_hat, wt, d_o, d_i, group, D, ld, flag,
+                                 stream));
+      GemmArgs g{};
+      g.M = d_o; g.N = d_i; g.K = d_i;
+      g.A = D; g.lda = ld;
+      g.B = H; g.ldb = d_i;      // H symmetric
+      g.C = Gm; g.ldc = ld;
+      QZ_TRY(launch_gemm_nt(EPI_STORE, g, stream));
+      QZ_TRY(launch_ls_propose(Gm, ld, H, d_i, codes, scales, d_o, group, bits, best_df, best_idx,
+                               stream));
+      QZ_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(counter), 1, 0u, stream));
+      QZ_TRY(launch_ls_accept(H, d_i, codes, scales, d_o, group, best_df, best_idx, counter,
+                              stream));
+    }
+    int32_t moved = 0;
+    QZ_HIP(hipMemcpyAsync(&moved, counter, sizeof(int32_t), hipMemcpyDeviceToHost, stream));
+    QZ_HIP(hipStreamSynchronize(stream));
+    if (moves_host) moves_host[t] = moved;
+    if (moved == 0) break;
+    steps = t + 1;
+  }
+  if (steps_host) *steps_host = steps;
+  uint32_t h = 0;
+  QZ_TRY(read_flag(flag, stream, &h));
+  if (h & FLAG_NONFINITE) return fail(QZ_ENONFINITE, "local_search: non-finite weight or grid");
   return QZ_OK;
 }
 

@@ -55,6 +55,7 @@ enum KernelKind : int {
   K_PACK,
   K_EIG,
   K_OBJECTIVE,
+  K_LSEARCH,
   K_KIND_COUNT
 };
 // Records an event pair around the enclosed launches when timing is enabled.
@@ -161,6 +162,16 @@ struct GemmArgs {
 };
 int gemm_tile_cols(int64_t N);   // ceil(N / 128): tile columns of the GEMM
 int launch_gemm_nt(int epi, const GemmArgs& a, hipStream_t s);
+
+// pairwise-swap local search (k_lsearch.hip)
+int ls_max_group();
+size_t ls_accept_lds(int64_t G);
+int launch_ls_propose(const float* Gm, int64_t ldg, const float* H, int64_t d_i,
+                      const uint8_t* codes, const float* scales, int64_t d_o, int group, int bits,
+                      float* best_df, int32_t* best_idx, hipStream_t s);
+int launch_ls_accept(const float* H, int64_t d_i, uint8_t* codes, const float* scales,
+                     int64_t d_o, int group, const float* best_df, const int32_t* best_idx,
+                     int32_t* counter, hipStream_t s);
 
 // bf16 Hessian (k_hessian.hip)
 size_t hessian_ws_bytes(int64_t n, int64_t d, int xt);

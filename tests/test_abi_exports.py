@@ -106,3 +106,23 @@ def test_objective_argument_errors(lib):
     assert lib.qz_objective(d, None, 0, None, None, None, 0, 16, 4, None, C.byref(out), d, need,
                             None) == _lib.QZ_OK
     assert out.value == 0.0
+
+
+def test_local_search_argument_errors(lib):
+    from post_weight_quantization_05_amd import _lib
+    d = C.c_void_p(4096)
+    g = _lib.QzGrid(C.sizeof(_lib.QzGrid), 3, 256, _lib.QZ_GRID_CALLER)
+    need = lib.qz_local_search_workspace(4, 512, 128)
+    assert need > 0
+    # groups wider than 128 columns
+    assert lib.qz_local_search(d, d, 0, 4, 512, C.byref(g), d, d, d, 3, None, None, d, 1 << 30,
+                               None) == _lib.QZ_EINVAL
+    g = _lib.QzGrid(C.sizeof(_lib.QzGrid), 3, 128, _lib.QZ_GRID_CALLER)
+    assert lib.qz_local_search(d, d, 0, 4, 512, C.byref(g), d, d, d, -1, None, None, d, need,
+                               None) == _lib.QZ_EINVAL
+    assert lib.qz_local_search(d, d, 0, 4, 512, C.byref(g), d, d, d, 3, None, None, d, need - 1,
+                               None) == _lib.QZ_EWORKSPACE
+    steps = C.c_int32(5)
+    assert lib.qz_local_search(d, d, 0, 4, 512, C.byref(g), d, d, d, 0, None, C.byref(steps), d,
+                               need, None) == _lib.QZ_OK
+    assert steps.value == 0
