@@ -77,6 +77,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=3072)
     ap.add_argument("--cpu-iters", type=int, default=40)
+    ap.add_argument("--ls-steps", type=int, default=64,
+                    help="step limit of the local search run on ADMM-Q's result (outside the timed steps)")
     ap.add_argument("--sweep", action="store_true",
                     help="one line per layer workload (1 warm-up and 1 timed step each), no CPU leg")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -304,9 +306,12 @@ def run_workload(args, name, steps, warmup, with_cpu):
     f_admm = q.qz_objective(H, W, ao["codes"], ao["scales"], ao["zeros"], group)
     cr, cs, cz = q.qz_rtn(W, bits, group)
     f_rtn = q.qz_objective(H, W, cr, cs, cz, group)
-    del V, lam, sig, ao
+    del V, lam, sig
     line["components"]["objective"] = {"rtn": f_rtn, "gptq": f_gptq, "admmq": f_admm,
                                        "admmq_over_gptq": round(f_admm / f_gptq, 4)}
+    line["components"]["local_search"] = local_search_leg(q, H, W, ao, bits, group, f_admm,
+                                                          f_gptq, args.ls_steps)
+    del ao
     if with_cpu:
         Xh = X[:16384].view(torch.int16).cpu().numpy().view(np.uint16)
         Wh = W[:args.cpu_rows].view(torch.int16).cpu().numpy().view(np.uint16)
@@ -314,6 +319,35 @@ def run_workload(args, name, steps, warmup, with_cpu):
     del X, W, H, ws_h, ws_g, ws_a
     torch.cuda.empty_cache()
     return line
+
+
+def local_search_leg(q, H, W, ao, bits, group, f_admm, f_gptq, max_steps):
+    """Pairwise-swap local search on ADMM-Q's result (outside the timed steps): steps,
+    moves per step, time per kernel kind and the objective it reaches."""
+    import torch
+    d_o, d_i = W.shape
+    ws = torch.empty(q.qz_local_search_workspace(d_o, d_i, group), dtype=torch.uint8,
+                     device=W.device)
+    codes = ao["codes"].clone()
+    q.qz_timing_read(reset=True)
+    q.qz_timing_enable(True)
+    b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    b.record()
+    steps, moves = q.qz_local_search(H, W, codes, ao["scales"], ao["zeros"], bits, group,
+                                     max_steps, ws=ws)
+    e.record()
+    torch.cuda.synchronize()
+    q.qz_timing_enable(False)
+    kt = q.qz_timing_read(reset=True)
+    f_ls = q.qz_objective(H, W, codes, ao["scales"], ao["zeros"], group)
+    out = {"steps": steps, "max_steps": max_steps, "moves_per_step": moves,
+           "call_ms": round(b.elapsed_time(e), 3),
+           "kernel_ms": {k: [v[0], round(v[1] / max(v[0], 1), 4)] for k, v in kt.items()
+                         if k.startswith("ls_")},
+           "f_after": f_ls, "after_over_admmq": round(f_ls / f_admm, 5),
+           "after_over_gptq": round(f_ls / f_gptq, 5)}
+    del ws, codes
+    return out
 
 
 SWEEP = ("attn_4096x4096_w3g128", "up_4096x12288_w3g128", "mlp_up_4096x12288_w2g128",

@@ -238,11 +238,13 @@ int qz_objective(const float* H, const void* W_hat, int32_t wt, const uint8_t* c
  * between positions of an output channel, evaluated by their direct effect on the
  * reconstruction error, in parallel).  The grid (scales, zeros) stays fixed.  Moves
  * are defined inside one group: one code +-1, or two codes j < k changed by a, b in
- * {-1, +1}.  Each step: the gradient (Q - W_hat) H on the matrix cores; every
- * (row, group) proposes its move with the smallest exact change of the objective
- * (qz_objective's f) if negative, ties to the smallest (j, k, a, b); each row accepts
- * proposals in ascending group order while the change plus the exact interaction with
- * the moves it already accepted stays negative, then applies them, so f never rises.
+ * {-1, +1}.  The gradient (Q - W_hat) H is formed once on the matrix cores (fp32) and
+ * kept up to date with the accepted moves.  Each step: every (row, group) proposes its
+ * move with the smallest exact change of the objective (qz_objective's f) if negative,
+ * ties to the smallest (j, k, a, b); each row accepts proposals in ascending group
+ * order while the change plus the exact interaction with the moves it already accepted
+ * stays negative, then applies them, so f never rises.  A row stops after a step that
+ * accepts none of its proposals; rows are independent.
  *   grid: bits and group_size (at most 128 columns; it divides d_i); scales, zeros
  *   [d_o x d_i/group_size] are inputs.  codes [d_o x d_i] u8 in/out.
  *   max_steps >= 0; the search stops after a step that accepts no move.

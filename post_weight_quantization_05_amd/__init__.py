@@ -265,7 +265,7 @@ def qz_timing_enable(on=True):
 
 def qz_timing_read(reset=True):
     """{kind name: (launches, total_ms)} of the launches recorded while timing was on."""
-    n = 16
+    n = 32
     launches = (C.c_int64 * n)()
     total = (C.c_double * n)()
     k = lib().qz_timing_read(launches, total, n, 1 if reset else 0)

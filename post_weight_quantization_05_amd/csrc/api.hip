@@ -65,7 +65,10 @@ size_t lsearch_ws(int64_t d_o, int64_t d_i, int64_t group) {
   c.take<float>(static_cast<size_t>(d_o) * round_up(d_i, 4));   // gradient D H
   c.take<float>(static_cast<size_t>(d_o) * G);                   // proposal change
   c.take<int32_t>(static_cast<size_t>(d_o) * G);                 // proposal index
-  c.take<int32_t>(1);                                             // accepted moves
+  c.take<int32_t>(2);                                             // moves, next rows
+  c.take<int32_t>(static_cast<size_t>(d_o));                      // active rows
+  c.take<int32_t>(static_cast<size_t>(d_o));                      // next active rows
+  c.take<float>(static_cast<size_t>(d_i));                        // pair-term bound per column
   return c.used;
 }
 
@@ -510,32 +513,51 @@ int qz_local_search(const float* H, const void* W_hat, int32_t wt, int64_t d_o, 
   float* Gm = cv.take<float>(static_cast<size_t>(d_o) * ld);
   float* best_df = cv.take<float>(static_cast<size_t>(d_o) * G);
   int32_t* best_idx = cv.take<int32_t>(static_cast<size_t>(d_o) * G);
-  int32_t* counter = cv.take<int32_t>(1);
+  int32_t* counters = cv.take<int32_t>(2);
+  int32_t* act = cv.take<int32_t>(static_cast<size_t>(d_o));
+  int32_t* next = cv.take<int32_t>(static_cast<size_t>(d_o));
+  float* hmax = cv.take<float>(static_cast<size_t>(d_i));
   QZ_TRY(launch_fill_u32(flag, 1, 0u, stream));
+  {
+    // the gradient of every row once, on the matrix cores; afterwards it is updated
+    // row by row with the accepted moves
+    ScopedTimer tm(K_LS_GRADIENT, stream);
+    QZ_TRY(launch_dequant_diff(codes, scales, zeros, W_hat, wt, d_o, d_i, group, D, ld, flag,
+                               stream));
+    GemmArgs g{};
+    g.M = d_o; g.N = d_i; g.K = d_i;
+    g.A = D; g.lda = ld;
+    g.B = H; g.ldb = d_i;      // H symmetric
+    g.C = Gm; g.ldc = ld;
+    QZ_TRY(launch_gemm_nt(EPI_STORE, g, stream));
+    QZ_TRY(launch_ls_iota(act, d_o, stream));
+    QZ_TRY(launch_ls_hmax(H, d_i, group, hmax, stream));
+  }
+  int64_t n_act = d_o;
   int steps = 0;
   for (int t = 0; t < max_steps; ++t) {
     {
-      ScopedTimer tm(K_LSEARCH, stream);
-      QZ_TRY(launch_dequant_diff(codes, scales, zeros, W_hat, wt, d_o, d_i, group, D, ld, flag,
-                                 stream));
-      GemmArgs g{};
-      g.M = d_o; g.N = d_i; g.K = d_i;
-      g.A = D; g.lda = ld;
-      g.B = H; g.ldb = d_i;      // H symmetric
-      g.C = Gm; g.ldc = ld;
-      QZ_TRY(launch_gemm_nt(EPI_STORE, g, stream));
-      QZ_TRY(launch_ls_propose(Gm, ld, H, d_i, codes, scales, d_o, group, bits, best_df, best_idx,
-                               stream));
-      QZ_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(counter), 1, 0u, stream));
-      QZ_TRY(launch_ls_accept(H, d_i, codes, scales, d_o, group, best_df, best_idx, counter,
-                              stream));
+      ScopedTimer tm(K_LS_PROPOSE, stream);
+      QZ_TRY(launch_ls_propose(Gm, ld, H, d_i, hmax, codes, scales, group, bits, act, n_act,
+                               best_df, best_idx, stream));
     }
-    int32_t moved = 0;
-    QZ_HIP(hipMemcpyAsync(&moved, counter, sizeof(int32_t), hipMemcpyDeviceToHost, stream));
+    {
+      ScopedTimer tm(K_LS_ACCEPT, stream);
+      QZ_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(counters), 2, 0u, stream));
+      QZ_TRY(launch_ls_accept(H, d_i, codes, scales, group, best_df, best_idx, act, n_act, Gm, ld,
+                              t + 1 < max_steps, next, counters, stream));
+    }
+    int32_t host_counters[2] = {0, 0};
+    QZ_HIP(hipMemcpyAsync(host_counters, counters, sizeof(host_counters), hipMemcpyDeviceToHost,
+                          stream));
     QZ_HIP(hipStreamSynchronize(stream));
-    if (moves_host) moves_host[t] = moved;
-    if (moved == 0) break;
+    if (moves_host) moves_host[t] = host_counters[0];
+    if (host_counters[0] == 0) break;
     steps = t + 1;
+    n_act = host_counters[1];
+    int32_t* tmp = act;
+    act = next;
+    next = tmp;
   }
   if (steps_host) *steps_host = steps;
   uint32_t h = 0;

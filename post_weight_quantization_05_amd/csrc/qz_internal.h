@@ -55,7 +55,9 @@ enum KernelKind : int {
   K_PACK,
   K_EIG,
   K_OBJECTIVE,
-  K_LSEARCH,
+  K_LS_GRADIENT,
+  K_LS_PROPOSE,
+  K_LS_ACCEPT,
   K_KIND_COUNT
 };
 // Records an event pair around the enclosed launches when timing is enabled.
@@ -166,12 +168,20 @@ int launch_gemm_nt(int epi, const GemmArgs& a, hipStream_t s);
 // pairwise-swap local search (k_lsearch.hip)
 int ls_max_group();
 size_t ls_accept_lds(int64_t G);
+int launch_ls_iota(int32_t* p, int64_t n, hipStream_t s);   // p[i] = i
+// hmax[c] = max |H[c][k]| over the other columns k of c's group
+int launch_ls_hmax(const float* H, int64_t d_i, int group, float* hmax, hipStream_t s);
+// best move per (act[a], group) for a < n_act -> best_df / best_idx [rows x G]
 int launch_ls_propose(const float* Gm, int64_t ldg, const float* H, int64_t d_i,
-                      const uint8_t* codes, const float* scales, int64_t d_o, int group, int bits,
-                      float* best_df, int32_t* best_idx, hipStream_t s);
-int launch_ls_accept(const float* H, int64_t d_i, uint8_t* codes, const float* scales,
-                     int64_t d_o, int group, const float* best_df, const int32_t* best_idx,
-                     int32_t* counter, hipStream_t s);
+                      const float* hmax, const uint8_t* codes, const float* scales, int group,
+                      int bits, const int32_t* act, int64_t n_act, float* best_df,
+                      int32_t* best_idx, hipStream_t s);
+// accept, apply, append moved rows to next_act (counters[0] += moves, counters[1] = slots)
+// and, when update, add the accepted moves' H rows to the gradient rows
+int launch_ls_accept(const float* H, int64_t d_i, uint8_t* codes, const float* scales, int group,
+                     const float* best_df, const int32_t* best_idx, const int32_t* act,
+                     int64_t n_act, float* Gm, int64_t ldg, bool update, int32_t* next_act,
+                     int32_t* counters, hipStream_t s);
 
 // bf16 Hessian (k_hessian.hip)
 size_t hessian_ws_bytes(int64_t n, int64_t d, int xt);

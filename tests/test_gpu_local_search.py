@@ -1,13 +1,16 @@
 """GPU parity of the pairwise-swap local search (qz_local_search) against the oracle.
 
 Both sides start from the oracle's round-to-nearest codes on the oracle's grid and H
-(no oracle input comes from the GPU).  The GPU runs one step per call; after every step
-the oracle takes the same step from the GPU's previous state and must reach the GPU's
-codes, adopting the GPU's choice only where its own decision margin (a proposal within
-the tolerance of the best, or a running change within the tolerance of zero) is below
-the fp32 resolution of the change: tol = 1e-4 s^2 max_j sum_k |H_jk| per row.  The
-whole run is also replayed by the oracle alone (with the same adoption rule) and must
-end on the same codes and objective."""
+(no oracle input comes from the GPU).  The library forms the gradient once and then
+updates it with the accepted moves, so the trajectory is observed by calls of k steps
+from the same start, k = 1, 2, ... (the search is deterministic per row): the codes after
+the k-step call are the state after step k.  For every step the oracle takes the same
+step from the GPU's previous state, with the gradient recomputed in fp64, and must reach
+the GPU's codes, adopting the GPU's choice only where its own decision margin (a
+proposal within the tolerance of the best, or a running change within the tolerance of
+zero) is below the fp32 resolution of the change: tol = 1e-4 s^2 max_j sum_k |H_jk| per
+row.  The whole run is also replayed by the oracle alone (with the same adoption rule)
+and must end on the same codes and objective."""
 import numpy as np
 import pytest
 
@@ -35,11 +38,13 @@ def _run(Hf, W_bits_or_f32, bits, group, steps, rows=None):
     rt = torch.from_numpy(r).cuda()
     snaps = [c0[r].astype(np.int64)]
     moved = []
-    for _ in range(steps):
-        n, mv = q.qz_local_search(Hd, Wd, cd, sd, zd, bits, group, 1)
-        moved.append(mv[0] if mv else 0)
+    for k in range(1, steps + 1):
+        cd.copy_(to_dev(c0))
+        n, mv = q.qz_local_search(Hd, Wd, cd, sd, zd, bits, group, k)
+        assert mv[:len(moved)] == moved[:len(mv)], "a longer run must repeat the shorter one"
+        moved = list(mv)
         snaps.append(to_host(cd[rt]).astype(np.int64))
-        if n == 0:
+        if n < k:
             break
     return Wf, s, z, snaps, moved
 
@@ -95,6 +100,40 @@ def test_local_search_full_layer_sampled_rows():
     Wf = qz_synth.bf16_bits_to_f32(W)
     _check("up_4096x12288_w3g128", Hf, Wf, s, z, cfg["bits"], cfg["group"], snaps, rows)
     assert moved[0] > 0
+
+
+def test_local_search_ragged_width():
+    """d_i not a multiple of 4 (the gradient update's scalar path), 3 groups of 30."""
+    X, W, _ = qz_synth.tiny_layer(3)
+    X, W = np.ascontiguousarray(X[:, :90]), np.ascontiguousarray(W[:, :90])
+    H, _ = hessian.hessian(X, 0.01)
+    Hf = H.astype(np.float32)
+    Wf, s, z, snaps, moved = _run(Hf, W, 3, 30, 40)
+    _check("tiny_90_w3g30", Hf, Wf, s, z, 3, 30, snaps, np.arange(W.shape[0]))
+    assert moved[0] > 0
+
+
+def test_local_search_long_run_matches_oracle():
+    """One call to convergence against the oracle's own run to convergence (no hints):
+    equal objective within 1e-4 and almost all codes equal."""
+    q = qz()
+    X, W, _ = qz_synth.tiny_layer(4)
+    H, _ = hessian.hessian(X, 0.01)
+    Hf = H.astype(np.float32)
+    s, z = grid.fit_grid_f32(W, 3, 32)
+    c0 = grid.rtn_f32(W, s, z, 3, 32).astype(np.uint8)
+    cd = to_dev(c0)
+    n, mv = q.qz_local_search(to_dev(Hf), to_dev(W), cd, to_dev(s), to_dev(z), 3, 32, 200)
+    assert 0 < n < 200 and mv[n] == 0
+    H64 = Hf.astype(np.float64)
+    out = ls.local_search(H64, W, c0, s, z, 3, 32, 200)
+    g = to_host(cd).astype(np.int64)
+    f_gpu = objective.row_objective(H64, W, grid.dequant(g, s, z, 32)).sum()
+    f_orc = objective.row_objective(H64, W, grid.dequant(out["codes"], s, z, 32)).sum()
+    report("local_search_long", steps=n, moves=int(sum(mv)), oracle_steps=int(out["steps"].max()),
+           f_rel=float(abs(f_gpu - f_orc) / f_orc), codes_equal=float(np.mean(g == out["codes"])))
+    assert abs(f_gpu - f_orc) <= TOL_OBJECTIVE * f_orc
+    assert np.mean(g == out["codes"]) >= 0.99
 
 
 def test_local_search_edge_cases():
