@@ -41,13 +41,13 @@ PEAK_FP64 = 78.6e12        # vector / matrix fp64, FLOP/s
 # SHA-256 of the kernel's source file at the time.  A kernel whose source has changed
 # since reports null.
 TRAFFIC = {
-    "gemm_admm_wupdate1": (3680.0e6, "k_gemm.hip",
-                           "86174034abd7fbd6c1ab491e98633463bde7a26039af9dd7ac87bd9b2f460929"),
-    "gemm_admm_wupdate2": (2955.0e6, "k_gemm.hip",
-                           "86174034abd7fbd6c1ab491e98633463bde7a26039af9dd7ac87bd9b2f460929"),
+    "gemm_admm_wupdate1": (3695.9e6, "k_gemm.hip",
+                           "6010e4b680bbf320e06de63e3097c75d686f1ec44846094578444eecf6f90d92"),
+    "gemm_admm_wupdate2": (2953.8e6, "k_gemm.hip",
+                           "6010e4b680bbf320e06de63e3097c75d686f1ec44846094578444eecf6f90d92"),
     "admm_project": (954.4e6, "k_admm.hip",
                      "98b0a5e274a588defa3bf1ac0a1a864e82c6008b35b54c3b7fb7e4ae8540c317"),
-    "hessian_gram_bf16": (17626.0e6, "k_hessian.hip",
+    "hessian_gram_bf16": (17023.2e6, "k_hessian.hip",
                           "abe54747eb0646e3cba1d9b30c147fbad51c04e3d4541bd970d7244b514870a0"),
 }
 TRAFFIC_WORKLOAD = "up_4096x12288_w3g128"
