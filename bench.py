@@ -77,7 +77,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=3072)
     ap.add_argument("--cpu-iters", type=int, default=40)
-    ap.add_argument("--ls-steps", type=int, default=64,
+    ap.add_argument("--ls-steps", type=int, default=256,
                     help="step limit of the local search run on ADMM-Q's result (outside the timed steps)")
     ap.add_argument("--sweep", action="store_true",
                     help="one line per layer workload (1 warm-up and 1 timed step each), no CPU leg")
@@ -311,7 +311,10 @@ def run_workload(args, name, steps, warmup, with_cpu):
                                        "admmq_over_gptq": round(f_admm / f_gptq, 4)}
     line["components"]["local_search"] = local_search_leg(q, H, W, ao, bits, group, f_admm,
                                                           f_gptq, args.ls_steps)
-    del ao
+    go = {"codes": gc, "scales": gs, "zeros": gz}
+    line["components"]["local_search_on_gptq"] = local_search_leg(q, H, W, go, bits, group, f_gptq,
+                                                                  f_gptq, args.ls_steps)
+    del ao, go
     if with_cpu:
         Xh = X[:16384].view(torch.int16).cpu().numpy().view(np.uint16)
         Wh = W[:args.cpu_rows].view(torch.int16).cpu().numpy().view(np.uint16)
@@ -321,30 +324,31 @@ def run_workload(args, name, steps, warmup, with_cpu):
     return line
 
 
-def local_search_leg(q, H, W, ao, bits, group, f_admm, f_gptq, max_steps):
-    """Pairwise-swap local search on ADMM-Q's result (outside the timed steps): steps,
-    moves per step, time per kernel kind and the objective it reaches."""
+def local_search_leg(q, H, W, start, bits, group, f_start, f_gptq, max_steps):
+    """Pairwise-swap local search on a solver's result `start` ({"codes", "scales",
+    "zeros"}, objective f_start), outside the timed steps: steps, moves per step, time per
+    kernel kind and the objective it reaches, relative to the start and to GPTQ's."""
     import torch
     d_o, d_i = W.shape
     ws = torch.empty(q.qz_local_search_workspace(d_o, d_i, group), dtype=torch.uint8,
                      device=W.device)
-    codes = ao["codes"].clone()
+    codes = start["codes"].clone()
     q.qz_timing_read(reset=True)
     q.qz_timing_enable(True)
     b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     b.record()
-    steps, moves = q.qz_local_search(H, W, codes, ao["scales"], ao["zeros"], bits, group,
+    steps, moves = q.qz_local_search(H, W, codes, start["scales"], start["zeros"], bits, group,
                                      max_steps, ws=ws)
     e.record()
     torch.cuda.synchronize()
     q.qz_timing_enable(False)
     kt = q.qz_timing_read(reset=True)
-    f_ls = q.qz_objective(H, W, codes, ao["scales"], ao["zeros"], group)
+    f_ls = q.qz_objective(H, W, codes, start["scales"], start["zeros"], group)
     out = {"steps": steps, "max_steps": max_steps, "moves_per_step": moves,
            "call_ms": round(b.elapsed_time(e), 3),
            "kernel_ms": {k: [v[0], round(v[1] / max(v[0], 1), 4)] for k, v in kt.items()
                          if k.startswith("ls_")},
-           "f_after": f_ls, "after_over_admmq": round(f_ls / f_admm, 5),
+           "f_after": f_ls, "after_over_start": round(f_ls / f_start, 5),
            "after_over_gptq": round(f_ls / f_gptq, 5)}
     del ws, codes
     return out

@@ -147,6 +147,60 @@ int qz_gptq(const float* H, const void* W_hat, int32_t wt, int64_t d_o, int64_t 
             uint8_t* codes, float* scales, uint8_t* zeros,
             void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* qz_gptq_noclip: qz_gptq without clipping (Babai page, technical summary, 2.3 and
+ * 3: the error bound of Theorem 5 holds when codes may take any integer value).  The
+ * code of a column is rint(w / s) + z unclamped (kept inside the int32 range), so the
+ * stored grid is the same but codes [d_o x d_i] are int32 and may leave [0, 2^b - 1].
+ * Arguments, workspace (qz_gptq_workspace), sync and errors as qz_gptq.          */
+int qz_gptq_noclip(const float* H, const void* W_hat, int32_t wt, int64_t d_o, int64_t d_i,
+                   const qz_grid* grid, int32_t B, const int32_t* perm,
+                   int32_t* codes, float* scales, uint8_t* zeros,
+                   void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------- orders and error bound --
+ * Babai page, technical summary, 2.3: without clipping the error of a row is
+ * bounded by a quarter of its squared scales weighted by the diagonal D of the
+ * LDL factorisation of the reordered Hessian (Theorem 5); the bound depends on the
+ * order; the min-pivot order (the smallest remaining diagonal at every LDL step)
+ * keeps the trace of D small and act order (descending diagonal) approximates it.
+ * Orders are quantization orders for qz_gptq's perm: perm[j] = the original column
+ * quantized j-th.  The LDL elimination runs in the reverse of the quantization
+ * order (the column quantized last is eliminated first).
+ *
+ * qz_order:
+ *   kind QZ_ORDER_ACT: columns by descending H_jj, ties to the smaller index.
+ *   kind QZ_ORDER_MIN_PIVOT: the reverse of the elimination order of a pivoted LDL
+ *     of H in fp64 that takes the smallest Schur-complement diagonal at every step
+ *     (among equal pivots the larger original index is eliminated first, so ties go
+ *     to the smaller index in quantization order, as in act order).  H must be
+ *     symmetric (the pivoted factorisation reads rows of the trailing matrix).
+ *   H [d_i x d_i] fp32; perm [d_i] int32 out.
+ *   pivots (device, nullable, MIN_PIVOT only): [d_i] fp64 out, the LDL pivot of the
+ *     column quantized j-th (the D of Theorem 5 for that order).
+ *   ws: qz_order_workspace(d_i, kind) bytes, 256-byte aligned (8 d_i^2 bytes for
+ *     MIN_PIVOT).  SYNC: QZ_ENONFINITE for a non-finite H, QZ_ENOTPD when a pivot
+ *     is <= 1e-12 of its column's diagonal.
+ *
+ * qz_error_bound: per row the Theorem 5 bound on the layer objective of
+ *   qz_objective without clipping, in quantization order perm (NULL = natural):
+ *     row_bound[r] = 1/8 sum_j D_j s(r, perm[j])^2
+ *   (the 1/4 of Theorem 5 times f's 1/2), D_j = the LDL pivot of the column quantized
+ *   j-th = 1 / R_jj^2 of qz_gptq's factor for that order (fp64 Cholesky of the
+ *   reversed, reordered H).  scales [d_o x d_i/group_size] (the grid the codes are
+ *   on).  row_bound (device, nullable) [d_o] fp64 out; out_host (host, nullable):
+ *   the sum over rows.  ws: qz_error_bound_workspace(d_o, d_i) bytes, 256-byte
+ *   aligned.  SYNC: QZ_EINVAL for a perm that is not a permutation, QZ_ENOTPD,
+ *   QZ_ENONFINITE as qz_gptq.                                                 */
+#define QZ_ORDER_ACT 1
+#define QZ_ORDER_MIN_PIVOT 2
+size_t qz_order_workspace(int64_t d_i, int32_t kind);
+int qz_order(const float* H, int64_t d_i, int32_t kind, int32_t* perm, double* pivots,
+             void* ws, size_t ws_bytes, hipStream_t stream);
+size_t qz_error_bound_workspace(int64_t d_o, int64_t d_i);
+int qz_error_bound(const float* H, int64_t d_i, const int32_t* perm, const float* scales,
+                   int64_t d_o, int32_t group_size, double* row_bound, double* out_host,
+                   void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* ----------------------------------------------------------------- ADMM-Q --
  * qz_admmq_prepare: Sigma = diag(H)^(-1/2), H~ = Sigma H Sigma and its
  * eigendecomposition H~ = V diag(Lambda) V^T (ADMM-Q summary, 2.: the
@@ -231,6 +285,12 @@ int qz_objective(const float* H, const void* W_hat, int32_t wt, const uint8_t* c
                  const float* scales, const uint8_t* zeros, int64_t d_o, int64_t d_i,
                  int32_t group_size, double* row_f, double* out_host, void* ws,
                  size_t ws_bytes, hipStream_t stream);
+/* qz_objective_i32: the same objective for int32 codes (qz_gptq_noclip's output);
+ * same workspace, sync and errors.                                            */
+int qz_objective_i32(const float* H, const void* W_hat, int32_t wt, const int32_t* codes,
+                     const float* scales, const uint8_t* zeros, int64_t d_o, int64_t d_i,
+                     int32_t group_size, double* row_f, double* out_host, void* ws,
+                     size_t ws_bytes, hipStream_t stream);
 
 /* ----------------------------------------------------------- local search --
  * Pairwise-swap local search after a solver (ADMM-Q summary, methodology, 2. key

@@ -146,6 +146,63 @@ def qz_gptq(H, W_hat, bits, group, B=128, perm=None, scales=None, zeros=None, ws
     return codes, scales, zeros
 
 
+def qz_gptq_noclip(H, W_hat, bits, group, B=128, perm=None, scales=None, zeros=None, ws=None):
+    """GPTQ without clipping: int32 codes (may leave [0, 2^bits - 1]) and the grid."""
+    torch = _torch()
+    _dev(H, "H")
+    _dev(W_hat, "W_hat")
+    d_o, d_i = W_hat.shape
+    caller = scales is not None
+    G = d_i // group if group > 0 and d_i % group == 0 else 0
+    if not caller:
+        scales = torch.empty((d_o, G), dtype=torch.float32, device=W_hat.device)
+        zeros = torch.empty((d_o, G), dtype=torch.uint8, device=W_hat.device)
+    codes = torch.empty((d_o, d_i), dtype=torch.int32, device=W_hat.device)
+    if perm is not None:
+        perm = _dev(perm.to(torch.int32), "perm")
+    if ws is None:
+        ws = _workspace(lib().qz_gptq_workspace(d_o, d_i, B), W_hat.device)
+    g = _grid(bits, group, caller)
+    _check(lib().qz_gptq_noclip(_ptr(H), _ptr(W_hat), _dtype_code(W_hat), d_o, d_i, C.byref(g),
+                                int(B), _ptr(perm), _ptr(codes), _ptr(scales), _ptr(zeros),
+                                _ptr(ws), ws.numel(), _stream()))
+    return codes, scales, zeros
+
+
+def qz_order(H, kind, pivots=False, ws=None):
+    """Quantization order for qz_gptq's perm: kind "act" or "min_pivot".  Returns perm
+    (int32) or, with pivots=True (min_pivot only), (perm, LDL pivots fp64)."""
+    torch = _torch()
+    _dev(H, "H")
+    d = H.shape[0]
+    k = {"act": _lib.QZ_ORDER_ACT, "min_pivot": _lib.QZ_ORDER_MIN_PIVOT}[kind]
+    perm = torch.empty(d, dtype=torch.int32, device=H.device)
+    piv = torch.empty(d, dtype=torch.float64, device=H.device) if pivots else None
+    if ws is None:
+        ws = _workspace(lib().qz_order_workspace(d, k), H.device)
+    _check(lib().qz_order(_ptr(H), d, k, _ptr(perm), _ptr(piv), _ptr(ws), ws.numel(), _stream()))
+    return (perm, piv) if pivots else perm
+
+
+def qz_error_bound(H, scales, group, perm=None, rows=False, ws=None):
+    """Theorem 5 bound on the no-clip layer objective in order perm: the total (float)
+    and, with rows=True, the per-row bounds (device fp64)."""
+    torch = _torch()
+    _dev(H, "H")
+    _dev(scales, "scales")
+    d_i = H.shape[0]
+    d_o = scales.shape[0]
+    if perm is not None:
+        perm = _dev(perm.to(torch.int32), "perm")
+    out = C.c_double(0.0)
+    rb = torch.empty(max(d_o, 1), dtype=torch.float64, device=H.device)
+    if ws is None:
+        ws = _workspace(lib().qz_error_bound_workspace(d_o, d_i), H.device)
+    _check(lib().qz_error_bound(_ptr(H), d_i, _ptr(perm), _ptr(scales), d_o, int(group), _ptr(rb),
+                                C.byref(out), _ptr(ws), ws.numel(), _stream()))
+    return (out.value, rb[:d_o]) if rows else out.value
+
+
 def qz_admmq_prepare(H):
     """(V, Lambda, sigma) with Sigma H Sigma = V diag(Lambda) V^T."""
     torch = _torch()
@@ -199,8 +256,9 @@ def qz_objective_workspace(d_o, d_i) -> int:
 
 
 def qz_objective(H, W_hat, codes, scales, zeros, group, rows=False, ws=None):
-    """f = 1/2 sum_r (q_r - w_r)^T H (q_r - w_r) for q = s (codes - z).  Returns the float
-    (and, with rows=True, the per-row fp64 objectives as a device tensor)."""
+    """f = 1/2 sum_r (q_r - w_r)^T H (q_r - w_r) for q = s (codes - z), codes uint8 or int32
+    (no-clip GPTQ).  Returns the float (and, with rows=True, the per-row fp64 objectives as
+    a device tensor)."""
     torch = _torch()
     for t, nm in ((H, "H"), (W_hat, "W_hat"), (codes, "codes"), (scales, "scales"), (zeros, "zeros")):
         _dev(t, nm)
@@ -209,9 +267,9 @@ def qz_objective(H, W_hat, codes, scales, zeros, group, rows=False, ws=None):
         ws = _workspace(lib().qz_objective_workspace(d_o, d_i), W_hat.device)
     row_f = torch.empty(d_o, dtype=torch.float64, device=W_hat.device) if rows else None
     out = C.c_double(0.0)
-    _check(lib().qz_objective(_ptr(H), _ptr(W_hat), _dtype_code(W_hat), _ptr(codes), _ptr(scales),
-                              _ptr(zeros), d_o, d_i, int(group), _ptr(row_f), C.byref(out),
-                              _ptr(ws), ws.numel(), _stream()))
+    fn = lib().qz_objective_i32 if codes.dtype == torch.int32 else lib().qz_objective
+    _check(fn(_ptr(H), _ptr(W_hat), _dtype_code(W_hat), _ptr(codes), _ptr(scales), _ptr(zeros), d_o,
+              d_i, int(group), _ptr(row_f), C.byref(out), _ptr(ws), ws.numel(), _stream()))
     return (out.value, row_f) if rows else out.value
 
 

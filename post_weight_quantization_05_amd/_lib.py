@@ -17,14 +17,19 @@ QZ_ADMM_WARM_START = 0x1
 QZ_ADMM_REFRESH_UNCLAMPED = 0x2
 QZ_ADMM_REFRESH_FROM_Z = 0x4
 QZ_ADMM_DUAL_NO_RESCALE = 0x8
+QZ_ORDER_ACT = 1
+QZ_ORDER_MIN_PIVOT = 2
 
 STATUS_NAMES = {0: "QZ_OK", -1: "QZ_EINVAL", -2: "QZ_ENOTPD", -3: "QZ_ENONFINITE", -4: "QZ_EHIP",
                 -5: "QZ_ESOLVER", -6: "QZ_EWORKSPACE"}
 
 # every entry point declared in include/qz.h
 EXPORTS = ("qz_hessian_workspace", "qz_build_hessian", "qz_rtn", "qz_gptq_workspace", "qz_gptq",
+           "qz_gptq_noclip", "qz_order_workspace", "qz_order", "qz_error_bound_workspace",
+           "qz_error_bound",
            "qz_admmq_prepare", "qz_admmq_workspace", "qz_admmq", "qz_objective_workspace",
-           "qz_objective", "qz_local_search_workspace", "qz_local_search", "qz_packed_words",
+           "qz_objective", "qz_objective_i32", "qz_local_search_workspace", "qz_local_search",
+           "qz_packed_words",
            "qz_pack",
            "qz_unpack", "qz_timing_enable", "qz_timing_read", "qz_timing_kind_name",
            "qz_last_error", "qz_abi_version")
@@ -54,12 +59,19 @@ _SIGS = {
     "qz_rtn": (C.c_int, [P, I32, I64, I64, C.POINTER(QzGrid), P, P, P, P]),
     "qz_gptq_workspace": (SZ, [I64, I64, I32]),
     "qz_gptq": (C.c_int, [P, P, I32, I64, I64, C.POINTER(QzGrid), I32, P, P, P, P, P, SZ, P]),
+    "qz_gptq_noclip": (C.c_int, [P, P, I32, I64, I64, C.POINTER(QzGrid), I32, P, P, P, P, P, SZ,
+                                 P]),
+    "qz_order_workspace": (SZ, [I64, I32]),
+    "qz_order": (C.c_int, [P, I64, I32, P, P, P, SZ, P]),
+    "qz_error_bound_workspace": (SZ, [I64, I64]),
+    "qz_error_bound": (C.c_int, [P, I64, P, P, I64, I32, P, P, P, SZ, P]),
     "qz_admmq_prepare": (C.c_int, [P, I64, P, P, P, P]),
     "qz_admmq_workspace": (SZ, [I64, I64, I32, I32]),
     "qz_admmq": (C.c_int, [P, P, P, P, I32, I64, I64, C.POINTER(QzGrid), C.POINTER(QzAdmm), P, P, P,
                            P, P, P, SZ, P]),
     "qz_objective_workspace": (SZ, [I64, I64]),
     "qz_objective": (C.c_int, [P, P, I32, P, P, P, I64, I64, I32, P, P, P, SZ, P]),
+    "qz_objective_i32": (C.c_int, [P, P, I32, P, P, P, I64, I64, I32, P, P, P, SZ, P]),
     "qz_local_search_workspace": (SZ, [I64, I64, I32]),
     "qz_local_search": (C.c_int, [P, P, I32, I64, I64, C.POINTER(QzGrid), P, P, P, I32, P, P, P,
                                   SZ, P]),

@@ -176,14 +176,16 @@ size_t qz_gptq_workspace(int64_t d_o, int64_t d_i, int32_t B) {
   return gptq_ws(d_o, d_i);
 }
 
-int qz_gptq(const float* H, const void* W_hat, int32_t wt, int64_t d_o, int64_t d_i,
-            const qz_grid* grid, int32_t B, const int32_t* perm, uint8_t* codes, float* scales,
-            uint8_t* zeros, void* ws, size_t ws_bytes, hipStream_t stream) {
+// GPTQ with u8 codes clamped to the grid (codes) or unclamped int32 codes (codes32).
+static int gptq_run(const float* H, const void* W_hat, int32_t wt, int64_t d_o, int64_t d_i,
+                    const qz_grid* grid, int32_t B, const int32_t* perm, uint8_t* codes,
+                    int32_t* codes32, float* scales, uint8_t* zeros, void* ws, size_t ws_bytes,
+                    hipStream_t stream) {
   if (!valid_dtype(wt)) return fail(QZ_EINVAL, "gptq: bad dtype");
   if (d_o < 0 || d_i < 1) return fail(QZ_EINVAL, "gptq: need d_o >= 0 and d_i >= 1");
   if (B < 1 || B > 128) return fail(QZ_EINVAL, "gptq: block size B must be in 1..128");
   QZ_TRY(check_grid(grid, d_i));
-  if (!H || (d_o > 0 && (!W_hat || !codes || !scales || !zeros)))
+  if (!H || (d_o > 0 && (!W_hat || (!codes && !codes32) || !scales || !zeros)))
     return fail(QZ_EINVAL, "gptq: null pointer");
   const size_t need = gptq_ws(d_o, d_i);
   if (ws_bytes < need || !ws) return fail(QZ_EWORKSPACE, "gptq: workspace too small");
@@ -231,7 +233,7 @@ int qz_gptq(const float* H, const void* W_hat, int32_t wt, int64_t d_o, int64_t 
     {
       ScopedTimer tm(K_GPTQ_BLOCK, stream);
       QZ_TRY(launch_gptq_block(Wf, ldw, d_o, a, b, Rt, ldr, scales, zeros, G, grid->group_size,
-                               grid->bits, perm, E, lde, codes, d_i, stream));
+                               grid->bits, perm, E, lde, codes, codes32, d_i, stream));
     }
     if (b < d_i) {
       GemmArgs g{};
@@ -247,6 +249,118 @@ int qz_gptq(const float* H, const void* W_hat, int32_t wt, int64_t d_o, int64_t 
       ScopedTimer tm(K_GEMM_GPTQ, stream);
       QZ_TRY(launch_gemm_nt(EPI_SUB, g, stream));
     }
+  }
+  return QZ_OK;
+}
+
+int qz_gptq(const float* H, const void* W_hat, int32_t wt, int64_t d_o, int64_t d_i,
+            const qz_grid* grid, int32_t B, const int32_t* perm, uint8_t* codes, float* scales,
+            uint8_t* zeros, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (d_o > 0 && !codes) return fail(QZ_EINVAL, "gptq: null pointer");
+  return gptq_run(H, W_hat, wt, d_o, d_i, grid, B, perm, codes, nullptr, scales, zeros, ws,
+                  ws_bytes, stream);
+}
+
+int qz_gptq_noclip(const float* H, const void* W_hat, int32_t wt, int64_t d_o, int64_t d_i,
+                   const qz_grid* grid, int32_t B, const int32_t* perm, int32_t* codes,
+                   float* scales, uint8_t* zeros, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (d_o > 0 && !codes) return fail(QZ_EINVAL, "gptq_noclip: null pointer");
+  return gptq_run(H, W_hat, wt, d_o, d_i, grid, B, perm, nullptr, codes, scales, zeros, ws,
+                  ws_bytes, stream);
+}
+
+// ------------------------------------------------------------------ orders, bound
+size_t qz_order_workspace(int64_t d_i, int32_t kind) {
+  if (d_i < 1 || (kind != QZ_ORDER_ACT && kind != QZ_ORDER_MIN_PIVOT)) return 0;
+  Carver c(nullptr);
+  c.take<uint32_t>(1);
+  c.used += order_ws_bytes(d_i, kind);
+  return c.used;
+}
+
+int qz_order(const float* H, int64_t d_i, int32_t kind, int32_t* perm, double* pivots, void* ws,
+             size_t ws_bytes, hipStream_t stream) {
+  if (d_i < 1) return fail(QZ_EINVAL, "order: d_i must be >= 1");
+  if (d_i > 0x7fffffff) return fail(QZ_EINVAL, "order: d_i too large");
+  if (kind != QZ_ORDER_ACT && kind != QZ_ORDER_MIN_PIVOT) return fail(QZ_EINVAL, "order: bad kind");
+  if (!H || !perm) return fail(QZ_EINVAL, "order: null pointer");
+  if (pivots && kind != QZ_ORDER_MIN_PIVOT)
+    return fail(QZ_EINVAL, "order: pivots are returned by the min-pivot order only");
+  const size_t need = qz_order_workspace(d_i, kind);
+  if (ws_bytes < need || !ws) return fail(QZ_EWORKSPACE, "order: workspace too small");
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0)
+    return fail(QZ_EWORKSPACE, "order: workspace must be 256-byte aligned");
+  set_error("");
+  Carver cv(ws);
+  uint32_t* flag = cv.take<uint32_t>(1);
+  void* rest = cv.base + cv.used;
+  QZ_TRY(launch_fill_u32(flag, 1, 0u, stream));
+  {
+    ScopedTimer tm(K_ORDER, stream);
+    if (kind == QZ_ORDER_ACT)
+      QZ_TRY(order_act(H, d_i, perm, rest, flag, stream));
+    else
+      QZ_TRY(order_min_pivot(H, d_i, perm, pivots, rest, flag, stream));
+  }
+  uint32_t h = 0;
+  QZ_TRY(read_flag(flag, stream, &h));
+  if (h & FLAG_NONFINITE) return fail(QZ_ENONFINITE, "order: non-finite H");
+  if (h & FLAG_NOTPD) return fail(QZ_ENOTPD, "order: H is not positive definite");
+  return QZ_OK;
+}
+
+size_t qz_error_bound_workspace(int64_t d_o, int64_t d_i) {
+  if (d_o < 0 || d_i < 1) return 0;
+  Carver c(nullptr);
+  c.take<uint32_t>(1);
+  c.take<double>(1);                                   // total
+  c.take<double>(static_cast<size_t>(d_i));            // D
+  c.take<double>(static_cast<size_t>(d_o > 0 ? d_o : 1));   // row bounds when not given
+  c.take<uint32_t>(static_cast<size_t>(d_i));          // permutation check
+  c.used += rfactor_ws_bytes(d_i);
+  return c.used;
+}
+
+int qz_error_bound(const float* H, int64_t d_i, const int32_t* perm, const float* scales,
+                   int64_t d_o, int32_t group_size, double* row_bound, double* out_host, void* ws,
+                   size_t ws_bytes, hipStream_t stream) {
+  if (d_o < 0 || d_i < 1) return fail(QZ_EINVAL, "error_bound: need d_o >= 0 and d_i >= 1");
+  if (group_size < 1 || d_i % group_size != 0)
+    return fail(QZ_EINVAL, "error_bound: group_size must divide d_i");
+  if (!H || (d_o > 0 && !scales)) return fail(QZ_EINVAL, "error_bound: null pointer");
+  const size_t need = qz_error_bound_workspace(d_o, d_i);
+  if (ws_bytes < need || !ws) return fail(QZ_EWORKSPACE, "error_bound: workspace too small");
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0)
+    return fail(QZ_EWORKSPACE, "error_bound: workspace must be 256-byte aligned");
+  set_error("");
+  Carver cv(ws);
+  uint32_t* flag = cv.take<uint32_t>(1);
+  double* total = cv.take<double>(1);
+  double* D = cv.take<double>(static_cast<size_t>(d_i));
+  double* rows = cv.take<double>(static_cast<size_t>(d_o > 0 ? d_o : 1));
+  uint32_t* counts = cv.take<uint32_t>(static_cast<size_t>(d_i));
+  void* rws = cv.base + cv.used;
+  QZ_TRY(launch_fill_u32(flag, 1, 0u, stream));
+  if (perm) {
+    QZ_TRY(launch_check_perm(perm, d_i, counts, flag, stream));
+    uint32_t hp = 0;
+    QZ_TRY(read_flag(flag, stream, &hp));
+    if (hp & FLAG_BADARG)
+      return fail(QZ_EINVAL, "error_bound: perm is not a permutation of 0..d_i-1");
+  }
+  {
+    ScopedTimer tm(K_ORDER, stream);
+    QZ_TRY(order_pivots(H, d_i, perm, D, rws, flag, stream));
+    QZ_TRY(launch_error_bound(D, perm, scales, d_o, d_i, group_size, row_bound ? row_bound : rows,
+                              total, stream));
+  }
+  uint32_t h = 0;
+  QZ_TRY(read_flag(flag, stream, &h));
+  if (h & FLAG_NONFINITE) return fail(QZ_ENONFINITE, "error_bound: non-finite H");
+  if (h & FLAG_NOTPD) return fail(QZ_ENOTPD, "error_bound: H is not positive definite");
+  if (out_host) {
+    QZ_HIP(hipMemcpyAsync(out_host, total, sizeof(double), hipMemcpyDeviceToHost, stream));
+    QZ_HIP(hipStreamSynchronize(stream));
   }
   return QZ_OK;
 }
@@ -429,15 +543,16 @@ size_t qz_objective_workspace(int64_t d_o, int64_t d_i) {
   return objective_ws(d_o, d_i);
 }
 
-int qz_objective(const float* H, const void* W_hat, int32_t wt, const uint8_t* codes,
-                 const float* scales, const uint8_t* zeros, int64_t d_o, int64_t d_i,
-                 int32_t group_size, double* row_f, double* out_host, void* ws, size_t ws_bytes,
-                 hipStream_t stream) {
+// The objective of u8 codes (codes) or int32 codes (codes32).
+static int objective_run(const float* H, const void* W_hat, int32_t wt, const uint8_t* codes,
+                         const int32_t* codes32, const float* scales, const uint8_t* zeros,
+                         int64_t d_o, int64_t d_i, int32_t group_size, double* row_f,
+                         double* out_host, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!valid_dtype(wt)) return fail(QZ_EINVAL, "objective: bad dtype");
   if (d_o < 0 || d_i < 1) return fail(QZ_EINVAL, "objective: need d_o >= 0 and d_i >= 1");
   if (group_size < 1 || d_i % group_size != 0)
     return fail(QZ_EINVAL, "objective: group_size must divide d_i");
-  if (!H || (d_o > 0 && (!W_hat || !codes || !scales || !zeros)))
+  if (!H || (d_o > 0 && (!W_hat || (!codes && !codes32) || !scales || !zeros)))
     return fail(QZ_EINVAL, "objective: null pointer");
   const size_t need = objective_ws(d_o, d_i);
   if (ws_bytes < need || !ws) return fail(QZ_EWORKSPACE, "objective: workspace too small");
@@ -458,8 +573,12 @@ int qz_objective(const float* H, const void* W_hat, int32_t wt, const uint8_t* c
   {
     ScopedTimer tm(K_OBJECTIVE, stream);
     QZ_TRY(launch_fill_u32(flag, 1, 0u, stream));
-    QZ_TRY(launch_dequant_diff(codes, scales, zeros, W_hat, wt, d_o, d_i, group_size, D, ld, flag,
-                               stream));
+    if (codes32)
+      QZ_TRY(launch_dequant_diff_i32(codes32, scales, zeros, W_hat, wt, d_o, d_i, group_size, D,
+                                     ld, flag, stream));
+    else
+      QZ_TRY(launch_dequant_diff(codes, scales, zeros, W_hat, wt, d_o, d_i, group_size, D, ld,
+                                 flag, stream));
     GemmArgs g{};
     g.M = d_o; g.N = d_i; g.K = d_i;
     g.A = D; g.lda = ld;
@@ -476,6 +595,24 @@ int qz_objective(const float* H, const void* W_hat, int32_t wt, const uint8_t* c
     if (h & FLAG_NONFINITE) return fail(QZ_ENONFINITE, "objective: non-finite weight or grid");
   }
   return QZ_OK;
+}
+
+int qz_objective(const float* H, const void* W_hat, int32_t wt, const uint8_t* codes,
+                 const float* scales, const uint8_t* zeros, int64_t d_o, int64_t d_i,
+                 int32_t group_size, double* row_f, double* out_host, void* ws, size_t ws_bytes,
+                 hipStream_t stream) {
+  if (d_o > 0 && !codes) return fail(QZ_EINVAL, "objective: null pointer");
+  return objective_run(H, W_hat, wt, codes, nullptr, scales, zeros, d_o, d_i, group_size, row_f,
+                       out_host, ws, ws_bytes, stream);
+}
+
+int qz_objective_i32(const float* H, const void* W_hat, int32_t wt, const int32_t* codes,
+                     const float* scales, const uint8_t* zeros, int64_t d_o, int64_t d_i,
+                     int32_t group_size, double* row_f, double* out_host, void* ws,
+                     size_t ws_bytes, hipStream_t stream) {
+  if (d_o > 0 && !codes) return fail(QZ_EINVAL, "objective: null pointer");
+  return objective_run(H, W_hat, wt, nullptr, codes, scales, zeros, d_o, d_i, group_size, row_f,
+                       out_host, ws, ws_bytes, stream);
 }
 
 // ------------------------------------------------------------------ local search

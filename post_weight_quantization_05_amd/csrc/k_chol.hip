@@ -256,16 +256,13 @@ size_t rfactor_ws_bytes(int64_t d) {
   return b;
 }
 
-int rfactor(const float* H, int64_t d, const int32_t* perm, float* Rt, int64_t ldr, void* ws,
-            uint32_t* flag, hipStream_t s) {
-  const int64_t dp = round_up(d, NB);
-  const int64_t nblk = dp / NB;
-  Carver cv(ws);
-  double* A = cv.take<double>(static_cast<size_t>(dp) * dp);
-  double* X = cv.take<double>(static_cast<size_t>(dp) * dp);
-  double* Dinv = cv.take<double>(static_cast<size_t>(nblk) * NB * NB);
-  double* diag0 = cv.take<double>(static_cast<size_t>(dp));
+namespace {
 
+// The reversed-order Cholesky in place: A (lower) = L with L L^T = J Hp J, plus the
+// inverses of the diagonal blocks in Dinv.
+int factor_reversed(const float* H, int64_t d, const int32_t* perm, double* A, int64_t dp,
+                    double* Dinv, double* diag0, uint32_t* flag, hipStream_t s) {
+  const int64_t nblk = dp / NB;
   init_reversed<<<grid_for(dp * dp), kThreads, 0, s>>>(H, d, perm, A, dp, diag0, flag);
   QZ_TRY(check_launch("rfactor.init"));
   for (int64_t k = 0; k < nblk; ++k) {
@@ -279,6 +276,31 @@ int rfactor(const float* H, int64_t d, const int32_t* perm, float* Rt, int64_t l
       QZ_TRY(check_launch("rfactor.trailing"));
     }
   }
+  return QZ_OK;
+}
+
+// D[j] = L[d-1-j][d-1-j]^2: the LDL pivot of the column quantized j-th.
+__global__ void pivots_from_factor(const double* __restrict__ A, int64_t lda, int64_t d,
+                                   double* __restrict__ D) {
+  const int64_t j = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (j >= d) return;
+  const double l = A[(d - 1 - j) * lda + (d - 1 - j)];
+  D[j] = l * l;
+}
+
+}  // namespace
+
+int rfactor(const float* H, int64_t d, const int32_t* perm, float* Rt, int64_t ldr, void* ws,
+            uint32_t* flag, hipStream_t s) {
+  const int64_t dp = round_up(d, NB);
+  const int64_t nblk = dp / NB;
+  Carver cv(ws);
+  double* A = cv.take<double>(static_cast<size_t>(dp) * dp);
+  double* X = cv.take<double>(static_cast<size_t>(dp) * dp);
+  double* Dinv = cv.take<double>(static_cast<size_t>(nblk) * NB * NB);
+  double* diag0 = cv.take<double>(static_cast<size_t>(dp));
+
+  QZ_TRY(factor_reversed(H, d, perm, A, dp, Dinv, diag0, flag, s));
   fill_identity<<<grid_for(dp * dp), kThreads, 0, s>>>(X, dp);
   QZ_TRY(check_launch("rfactor.fill"));
   for (int64_t i = 0; i < nblk; ++i) {
@@ -292,6 +314,20 @@ int rfactor(const float* H, int64_t d, const int32_t* perm, float* Rt, int64_t l
   }
   extract_rt<<<grid_for(d * d), kThreads, 0, s>>>(X, dp, d, Rt, ldr);
   return check_launch("rfactor.extract");
+}
+
+int order_pivots(const float* H, int64_t d, const int32_t* perm, double* D, void* ws,
+                 uint32_t* flag, hipStream_t s) {
+  const int64_t dp = round_up(d, NB);
+  const int64_t nblk = dp / NB;
+  Carver cv(ws);
+  double* A = cv.take<double>(static_cast<size_t>(dp) * dp);
+  cv.take<double>(static_cast<size_t>(dp) * dp);   // (the inverse's buffer, unused here)
+  double* Dinv = cv.take<double>(static_cast<size_t>(nblk) * NB * NB);
+  double* diag0 = cv.take<double>(static_cast<size_t>(dp));
+  QZ_TRY(factor_reversed(H, d, perm, A, dp, Dinv, diag0, flag, s));
+  pivots_from_factor<<<grid_for(d), kThreads, 0, s>>>(A, dp, d, D);
+  return check_launch("order_pivots");
 }
 
 }  // namespace qz

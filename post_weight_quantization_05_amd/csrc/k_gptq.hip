@@ -37,12 +37,21 @@ __device__ __forceinline__ float quad_bcast(float v, int owner) {
   return __int_as_float(r);
 }
 
+// Unclamped code rint(x / s) + z, kept inside the int32 range.
+__device__ __forceinline__ float quant_code_noclip(float x, float s, float z) {
+  const float u = __builtin_rintf(x / s) + z;
+  return fminf(fmaxf(u, -2147483648.0f), 2147483520.0f);
+}
+
+// NOCLIP: codes are not clamped to [0, 2^b - 1] (the Babai page's no-clipping regime);
+// they stay in registers (one per owned column) and are written as int32 to codes32.
+template <bool NOCLIP>
 __global__ __launch_bounds__(kThreads) void gptq_block_kernel(
     float* __restrict__ W, int64_t ldw, int64_t d_o, int64_t a, int w,
     const float* __restrict__ Rt, int64_t ldr, const float* __restrict__ scales,
     const uint8_t* __restrict__ zeros, int64_t G, int group, float maxq,
     const int32_t* __restrict__ perm, float* __restrict__ E, int64_t lde,
-    uint8_t* __restrict__ codes, int64_t d_i) {
+    uint8_t* __restrict__ codes, int32_t* __restrict__ codes32, int64_t d_i) {
   __shared__ __attribute__((aligned(16))) float Rb[MAXB][4][PER];   // Rb[j][q][i] = R[a+j][a+q+4i]
   __shared__ __attribute__((aligned(8))) float2 sz[ROWS][MAXB];      // (scale, zero) of (row, column)
   __shared__ float rinv[MAXB];
@@ -76,6 +85,7 @@ __global__ __launch_bounds__(kThreads) void gptq_block_kernel(
   }
 
   float wr[PER];
+  float cr[NOCLIP ? PER : 1];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int c = q + 4 * i;
@@ -91,12 +101,15 @@ __global__ __launch_bounds__(kThreads) void gptq_block_kernel(
     // every lane rounds its own value of slot `slot`; only the owner's is used
     const float x = wr[slot];
     const float2 g = sz[rl][4 * slot + q];
-    const float c = quant_code(x, g.x, g.y, maxq);
+    const float c = NOCLIP ? quant_code_noclip(x, g.x, g.y) : quant_code(x, g.x, g.y, maxq);
     const float qv = g.x * (c - g.y);
     const float err = (x - qv) * rinv[j];
     if (q == owner) {
       wr[slot] = err;
-      cs[rl][j] = static_cast<uint8_t>(c);
+      if constexpr (NOCLIP)
+        cr[slot] = c;
+      else
+        cs[rl][j] = static_cast<uint8_t>(c);
     }
     const float e = quad_bcast(err, owner);
     const float* rrow = &Rb[j][q][0];
@@ -117,9 +130,19 @@ __global__ __launch_bounds__(kThreads) void gptq_block_kernel(
       const int c = q + 4 * i;
       if (c < w) E[row * lde + c] = wr[i];
     }
-    for (int c = q; c < w; c += 4) {
-      const int64_t oc = perm ? perm[a + c] : a + c;
-      codes[row * d_i + oc] = cs[rl][c];
+    if constexpr (NOCLIP) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int c = q + 4 * i;
+        if (c >= w) continue;
+        const int64_t oc = perm ? perm[a + c] : a + c;
+        codes32[row * d_i + oc] = static_cast<int32_t>(cr[i]);
+      }
+    } else {
+      for (int c = q; c < w; c += 4) {
+        const int64_t oc = perm ? perm[a + c] : a + c;
+        codes[row * d_i + oc] = cs[rl][c];
+      }
     }
   }
 }
@@ -129,13 +152,20 @@ __global__ __launch_bounds__(kThreads) void gptq_block_kernel(
 int launch_gptq_block(float* W, int64_t ldw, int64_t d_o, int64_t a, int64_t b, const float* Rt,
                       int64_t ldr, const float* scales, const uint8_t* zeros, int64_t n_groups,
                       int group, int bits, const int32_t* perm, float* E, int64_t lde,
-                      uint8_t* codes, int64_t d_i, hipStream_t s) {
+                      uint8_t* codes, int32_t* codes32, int64_t d_i, hipStream_t s) {
   const int w = static_cast<int>(b - a);
   if (w <= 0 || w > MAXB) return fail(QZ_EINVAL, "gptq block width out of range");
+  if (!codes == !codes32) return fail(QZ_EINVAL, "gptq block: exactly one code output");
   const float maxq = static_cast<float>((1 << bits) - 1);
   const unsigned nb = static_cast<unsigned>(ceil_div(d_o, ROWS));
-  gptq_block_kernel<<<nb, kThreads, 0, s>>>(W, ldw, d_o, a, w, Rt, ldr, scales, zeros, n_groups,
-                                            group, maxq, perm, E, lde, codes, d_i);
+  if (codes32)
+    gptq_block_kernel<true><<<nb, kThreads, 0, s>>>(W, ldw, d_o, a, w, Rt, ldr, scales, zeros,
+                                                    n_groups, group, maxq, perm, E, lde, nullptr,
+                                                    codes32, d_i);
+  else
+    gptq_block_kernel<false><<<nb, kThreads, 0, s>>>(W, ldw, d_o, a, w, Rt, ldr, scales, zeros,
+                                                     n_groups, group, maxq, perm, E, lde, codes,
+                                                     nullptr, d_i);
   return check_launch("gptq_block");
 }
 

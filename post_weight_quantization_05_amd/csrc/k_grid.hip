@@ -209,9 +209,9 @@ __global__ __launch_bounds__(kThreads) void zero_u32_kernel(uint32_t* __restrict
 }
 
 // D = s (C - z) - W_hat per element (the dequantized weights' error), fp32.
-template <int WT>
+template <int WT, typename CT>
 __global__ __launch_bounds__(kThreads) void dequant_diff_kernel(
-    const uint8_t* __restrict__ codes, const float* __restrict__ scales,
+    const CT* __restrict__ codes, const float* __restrict__ scales,
     const uint8_t* __restrict__ zeros, const void* __restrict__ W, int64_t rows, int64_t cols,
     int group, float* __restrict__ out, int64_t ldo, uint32_t* __restrict__ flag) {
   const int64_t total = rows * cols;
@@ -329,19 +329,32 @@ int launch_to_f32(const void* W, int wt, int64_t rows, int64_t cols, const int32
   return check_launch("to_f32");
 }
 
-int launch_dequant_diff(const uint8_t* codes, const float* scales, const uint8_t* zeros,
-                        const void* W, int wt, int64_t rows, int64_t cols, int group, float* out,
-                        int64_t ldo, uint32_t* flag, hipStream_t s) {
+template <typename CT>
+static int dequant_diff_any(const CT* codes, const float* scales, const uint8_t* zeros,
+                            const void* W, int wt, int64_t rows, int64_t cols, int group,
+                            float* out, int64_t ldo, uint32_t* flag, hipStream_t s) {
   const int64_t n = rows * cols;
   if (n == 0) return QZ_OK;
   const int nb = blocks_for(n, kThreads * 4, 65536);
   if (wt == QZ_BF16)
-    dequant_diff_kernel<QZ_BF16><<<nb, kThreads, 0, s>>>(codes, scales, zeros, W, rows, cols, group,
-                                                          out, ldo, flag);
+    dequant_diff_kernel<QZ_BF16, CT><<<nb, kThreads, 0, s>>>(codes, scales, zeros, W, rows, cols,
+                                                              group, out, ldo, flag);
   else
-    dequant_diff_kernel<QZ_F32><<<nb, kThreads, 0, s>>>(codes, scales, zeros, W, rows, cols, group,
-                                                         out, ldo, flag);
+    dequant_diff_kernel<QZ_F32, CT><<<nb, kThreads, 0, s>>>(codes, scales, zeros, W, rows, cols,
+                                                             group, out, ldo, flag);
   return check_launch("dequant_diff");
+}
+
+int launch_dequant_diff(const uint8_t* codes, const float* scales, const uint8_t* zeros,
+                        const void* W, int wt, int64_t rows, int64_t cols, int group, float* out,
+                        int64_t ldo, uint32_t* flag, hipStream_t s) {
+  return dequant_diff_any(codes, scales, zeros, W, wt, rows, cols, group, out, ldo, flag, s);
+}
+
+int launch_dequant_diff_i32(const int32_t* codes, const float* scales, const uint8_t* zeros,
+                            const void* W, int wt, int64_t rows, int64_t cols, int group,
+                            float* out, int64_t ldo, uint32_t* flag, hipStream_t s) {
+  return dequant_diff_any(codes, scales, zeros, W, wt, rows, cols, group, out, ldo, flag, s);
 }
 
 int launch_rowsum_half(const double* dpart, int64_t rows, int64_t tcols, double* row_f,

@@ -58,6 +58,7 @@ enum KernelKind : int {
   K_LS_GRADIENT,
   K_LS_PROPOSE,
   K_LS_ACCEPT,
+  K_ORDER,
   K_KIND_COUNT
 };
 // Records an event pair around the enclosed launches when timing is enabled.
@@ -136,6 +137,10 @@ int launch_check_finite_f32(const float* p, int64_t n, uint32_t* flag, hipStream
 int launch_dequant_diff(const uint8_t* codes, const float* scales, const uint8_t* zeros,
                         const void* W, int wt, int64_t rows, int64_t cols, int group, float* out,
                         int64_t ldo, uint32_t* flag, hipStream_t s);
+// the same for int32 codes (unclamped GPTQ codes)
+int launch_dequant_diff_i32(const int32_t* codes, const float* scales, const uint8_t* zeros,
+                            const void* W, int wt, int64_t rows, int64_t cols, int group,
+                            float* out, int64_t ldo, uint32_t* flag, hipStream_t s);
 // row_f[r] = 0.5 * sum_t dpart[r][t]; total = sum_r row_f[r] (fixed order, one workgroup)
 int launch_rowsum_half(const double* dpart, int64_t rows, int64_t tcols, double* row_f,
                        double* total, hipStream_t s);
@@ -189,18 +194,32 @@ int hessian_build(const void* X, int xt, int64_t n, int64_t d, float damp, uint3
                   float* H, float* diag, float* sigma, float* lambda_out, void* ws,
                   size_t ws_bytes, hipStream_t s);
 
+// orders and the error bound (k_order.hip)
+size_t order_ws_bytes(int64_t n, int kind);
+int order_act(const float* H, int64_t n, int32_t* perm, void* ws, uint32_t* flag, hipStream_t s);
+int order_min_pivot(const float* H, int64_t n, int32_t* perm, double* pivots, void* ws,
+                    uint32_t* flag, hipStream_t s);
+// row_bound[r] = 1/8 sum_j D[j] s(r, perm[j] / group)^2; *total = fixed-order row sum
+int launch_error_bound(const double* D, const int32_t* perm, const float* scales, int64_t d_o,
+                       int64_t d_i, int group, double* row_bound, double* total, hipStream_t s);
+
 // fp64 Cholesky / inverse factor (k_chol.hip)
 size_t rfactor_ws_bytes(int64_t d);
 // Rt (lower, row-major, ld ldr) = R^T where R is upper with R^T R = Hp^{-1},
 // Hp = H[perm][:, perm] (perm may be null).  Sets FLAG_NOTPD / FLAG_NONFINITE.
 int rfactor(const float* H, int64_t d, const int32_t* perm, float* Rt, int64_t ldr, void* ws,
             uint32_t* flag, hipStream_t s);
+// D[j] (fp64, [d]) = LDL pivot of the column quantized j-th in the order perm (null =
+// natural): the diagonal of Hp reordered so the column quantized last is eliminated
+// first, i.e. 1 / R_jj^2 of GPTQ's factor.  Same workspace and flags as rfactor.
+int order_pivots(const float* H, int64_t d, const int32_t* perm, double* D, void* ws,
+                 uint32_t* flag, hipStream_t s);
 
 // GPTQ in-block column kernel (k_gptq.hip)
 int launch_gptq_block(float* W, int64_t ldw, int64_t d_o, int64_t a, int64_t b, const float* Rt,
                       int64_t ldr, const float* scales, const uint8_t* zeros, int64_t n_groups,
                       int group, int bits, const int32_t* perm, float* E, int64_t lde,
-                      uint8_t* codes, int64_t d_i, hipStream_t s);
+                      uint8_t* codes, int32_t* codes32, int64_t d_i, hipStream_t s);
 
 // ADMM kernels (k_admm.hip)
 struct AdmmProj {

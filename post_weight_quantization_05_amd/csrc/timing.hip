@@ -24,7 +24,7 @@ const char* const kNames[K_KIND_COUNT] = {
     "hessian_gram_bf16", "hessian_finish", "rfactor_fp64", "gptq_block", "gemm_gptq_trailing",
     "gemm_admm_setup", "gemm_admm_wupdate1", "gemm_admm_wupdate2", "admm_project", "admm_other",
     "grid_rtn", "pack", "eig_prepare", "objective", "ls_gradient", "ls_propose",
-    "ls_accept"};
+    "ls_accept", "order"};
 
 hipEvent_t take_event() {
   if (!g_pool.empty()) {

@@ -126,3 +126,37 @@ def test_local_search_argument_errors(lib):
     assert lib.qz_local_search(d, d, 0, 4, 512, C.byref(g), d, d, d, 0, None, C.byref(steps), d,
                                need, None) == _lib.QZ_OK
     assert steps.value == 0
+
+
+def test_order_bound_noclip_argument_errors(lib):
+    from post_weight_quantization_05_amd import _lib
+    p = C.c_void_p(256)
+    assert lib.qz_order_workspace(128, 3) == 0
+    assert lib.qz_order_workspace(128, _lib.QZ_ORDER_MIN_PIVOT) >= 8 * 128 * 128
+    assert 0 < lib.qz_order_workspace(128, _lib.QZ_ORDER_ACT) < 8 * 128 * 128
+    ws = lib.qz_order_workspace(128, _lib.QZ_ORDER_ACT)
+    assert lib.qz_order(p, 128, 3, p, None, p, ws, None) == _lib.QZ_EINVAL
+    assert lib.qz_order(None, 128, _lib.QZ_ORDER_ACT, p, None, p, ws, None) == _lib.QZ_EINVAL
+    assert lib.qz_order(p, 0, _lib.QZ_ORDER_ACT, p, None, p, ws, None) == _lib.QZ_EINVAL
+    # pivots come only with the min-pivot order
+    assert lib.qz_order(p, 128, _lib.QZ_ORDER_ACT, p, p, p, ws, None) == _lib.QZ_EINVAL
+    assert b"pivots" in lib.qz_last_error()
+    assert lib.qz_order(p, 128, _lib.QZ_ORDER_ACT, p, None, p, ws - 1, None) == _lib.QZ_EWORKSPACE
+    assert lib.qz_order(p, 128, _lib.QZ_ORDER_ACT, p, None, C.c_void_p(264), ws,
+                        None) == _lib.QZ_EWORKSPACE
+    wb = lib.qz_error_bound_workspace(8, 128)
+    assert wb > 0 and lib.qz_error_bound_workspace(-1, 128) == 0
+    assert lib.qz_error_bound(p, 128, None, p, 8, 100, None, None, p, wb, None) == _lib.QZ_EINVAL
+    assert b"group" in lib.qz_last_error()
+    assert lib.qz_error_bound(p, 128, None, None, 8, 32, None, None, p, wb, None) == _lib.QZ_EINVAL
+    assert lib.qz_error_bound(p, 128, None, p, 8, 32, None, None, p, wb - 1,
+                              None) == _lib.QZ_EWORKSPACE
+    g = _lib.QzGrid(C.sizeof(_lib.QzGrid), 3, 32, 0)
+    wg = lib.qz_gptq_workspace(8, 128, 32)
+    assert lib.qz_gptq_noclip(p, p, 0, 8, 128, C.byref(g), 32, None, None, p, p, p, wg,
+                              None) == _lib.QZ_EINVAL
+    assert lib.qz_gptq_noclip(p, p, 0, 8, 128, C.byref(g), 129, None, p, p, p, p, wg,
+                              None) == _lib.QZ_EINVAL
+    wo = lib.qz_objective_workspace(8, 128)
+    assert lib.qz_objective_i32(p, p, 0, None, p, p, 8, 128, 32, None, None, p, wo,
+                                None) == _lib.QZ_EINVAL
