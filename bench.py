@@ -311,6 +311,7 @@ def run_workload(args, name, steps, warmup, with_cpu):
                                        "admmq_over_gptq": round(f_admm / f_gptq, 4)}
     line["components"]["local_search"] = local_search_leg(q, H, W, ao, bits, group, f_admm,
                                                           f_gptq, args.ls_steps)
+    line["components"]["orders"] = orders_leg(q, H, W, bits, group, B)
     go = {"codes": gc, "scales": gs, "zeros": gz}
     line["components"]["local_search_on_gptq"] = local_search_leg(q, H, W, go, bits, group, f_gptq,
                                                                   f_gptq, args.ls_steps)
@@ -351,6 +352,34 @@ def local_search_leg(q, H, W, start, bits, group, f_start, f_gptq, max_steps):
            "f_after": f_ls, "after_over_start": round(f_ls / f_start, 5),
            "after_over_gptq": round(f_ls / f_gptq, 5)}
     del ws, codes
+    return out
+
+
+def orders_leg(q, H, W, bits, group, B):
+    """Quantization orders (outside the timed steps): time of each order, and per order
+    (natural, act, min-pivot) the Theorem 5 bound on the no-clip objective, GPTQ's
+    objective without clipping and with it."""
+    import torch
+    out = {}
+    perms = {"natural": None}
+    for kind in ("act", "min_pivot"):
+        b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b.record()
+        perms[kind] = q.qz_order(H, kind)
+        e.record()
+        torch.cuda.synchronize()
+        out[f"{kind}_order_ms"] = round(b.elapsed_time(e), 3)
+    for kind, perm in perms.items():
+        cn, sn, zn = q.qz_gptq_noclip(H, W, bits, group, B, perm=perm)
+        f_noclip = q.qz_objective(H, W, cn, sn, zn, group)
+        bound = q.qz_error_bound(H, sn, group, perm=perm)
+        off = float(((cn < 0) | (cn > (1 << bits) - 1)).float().mean().item())
+        del cn
+        cg, sg, zg = q.qz_gptq(H, W, bits, group, B, perm=perm)
+        f_clip = q.qz_objective(H, W, cg, sg, zg, group)
+        del cg, sg, zg, sn, zn
+        out[kind] = {"bound": bound, "gptq_noclip": f_noclip, "noclip_over_bound": round(f_noclip / bound, 4),
+                     "noclip_off_grid": round(off, 5), "gptq": f_clip}
     return out
 
 

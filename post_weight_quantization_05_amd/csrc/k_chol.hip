@@ -282,10 +282,11 @@ int factor_reversed(const float* H, int64_t d, const int32_t* perm, double* A, i
 // D[j] = L[d-1-j][d-1-j]^2: the LDL pivot of the column quantized j-th.
 __global__ void pivots_from_factor(const double* __restrict__ A, int64_t lda, int64_t d,
                                    double* __restrict__ D) {
-  const int64_t j = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (j >= d) return;
-  const double l = A[(d - 1 - j) * lda + (d - 1 - j)];
-  D[j] = l * l;
+  for (int64_t j = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; j < d;
+       j += (int64_t)gridDim.x * blockDim.x) {
+    const double l = A[(d - 1 - j) * lda + (d - 1 - j)];
+    D[j] = l * l;
+  }
 }
 
 }  // namespace

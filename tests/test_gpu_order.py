@@ -134,6 +134,41 @@ def test_error_bound_matches_oracle(which):
     assert abs(total - ref.sum()) <= 1e-8 * ref.sum()
 
 
+def test_error_bound_full_layer_size():
+    """The 4096-column layer: per-row bounds of sampled rows in the natural, act and
+    min-pivot orders against pivots from a LAPACK Cholesky of H reordered with the
+    column quantized last first (the oracle's plain elimination is too slow here)."""
+    import torch
+    q = qz()
+    cfg = qz_synth.WORKLOADS["up_4096x12288_w3g128"]
+    X = qz_synth.calib_bf16_torch(cfg["seed"], 16384, cfg["d_i"], cfg["p_out"], cfg["f_out"])
+    Xh = to_host(X)
+    del X
+    torch.cuda.empty_cache()
+    H64, _ = hessian.hessian(Xh, cfg["damp"])
+    Hf = H64.astype(np.float32)
+    H64 = Hf.astype(np.float64)
+    W = qz_synth.weights_bf16(cfg["seed"], cfg["d_o"], cfg["d_i"])
+    Wf = qz_synth.bf16_bits_to_f32(W)
+    s, _ = grid.fit_grid_f32(Wf, cfg["bits"], cfg["group"])
+    Hd, sd = to_dev(Hf), to_dev(s)
+    rows = sample_rows(cfg["d_o"])
+    n, g = cfg["d_i"], cfg["group"]
+    totals = {}
+    for which in ("natural", "act", "min_pivot"):
+        perm_d = None if which == "natural" else q.qz_order(Hd, which)
+        perm = np.arange(n) if perm_d is None else to_host(perm_d).astype(np.int64)
+        total, b = q.qz_error_bound(Hd, sd, g, perm=perm_d, rows=True)
+        elim = perm[::-1]
+        D = (np.diag(np.linalg.cholesky(H64[np.ix_(elim, elim)])) ** 2)[::-1]
+        sc = s[:, perm // g].astype(np.float64)
+        ref = 0.125 * (sc * sc) @ D
+        np.testing.assert_allclose(to_host(b)[rows], ref[rows], rtol=1e-8)
+        assert abs(total - ref.sum()) <= 1e-8 * ref.sum()
+        totals[which] = total
+    report("error_bound_full", **totals)
+
+
 @pytest.mark.parametrize("which,bits,group,d_o,d_i", [("natural", 2, 32, 64, 128),
                                                       ("act", 2, 8, 70, 200),
                                                       ("min_pivot", 3, 64, 33, 192),
