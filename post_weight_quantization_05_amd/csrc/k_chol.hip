@@ -54,18 +54,35 @@ __global__ __launch_bounds__(kThreads) void init_reversed(const float* __restric
   if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(flag, FLAG_NONFINITE);
 }
 
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const int lo = __builtin_amdgcn_readlane(__double2loint(v), l);
+  const int hi = __builtin_amdgcn_readlane(__double2hiint(v), l);
+  return __hiloint2double(hi, lo);
+}
+
+// 1 / sqrt(p) for p > 0: the hardware estimate refined by two Newton steps
+// y <- y (3 - p y^2) / 2 (each step squares the relative error).
+__device__ __forceinline__ double rsqrt_f64(double p) {
+  double y = __builtin_amdgcn_rsq(p);
+  y = y * (1.5 - 0.5 * p * y * y);
+  y = y * (1.5 - 0.5 * p * y * y);
+  return y;
+}
+
 // Factor diagonal block k in place (lower) and write its inverse to Dinv[k].
 // One wavefront: lane i holds row i of the block in registers during the factorisation
-// (column j is scaled by the pivot's reciprocal square root, written to LDS and read
-// back by every lane as uniform broadcasts for the rank-one update of the rows below),
-// and column i of the inverse during the forward substitution (rows of L come from LDS
-// as uniform reads, the diagonal's reciprocals are formed up front).  All exchanges
-// stay within the wavefront.
+// (all 64 loads of a row in flight at once).  Per column j the pivot is broadcast
+// from lane j (readlane) and every lane forms its reciprocal square root; the new
+// column goes to LDS twice, row-major (Ls, for the inverse) and column-major (Lc, so the
+// rank-one update of the rows below reads one contiguous run of uniform broadcasts).
+// The inverse is formed by forward substitution with lane i holding column i, each sum
+// split over four independent partial sums.
 __global__ __launch_bounds__(NB) void diag_block(double* __restrict__ A, int64_t lda, int64_t k,
                                                  const double* __restrict__ diag0,
                                                  double* __restrict__ Dinv,
                                                  uint32_t* __restrict__ flag) {
-  __shared__ double Ls[NB][NB + 2];   // rows of L (even stride: 16-byte pair reads)
+  __shared__ double Ls[NB][NB + 2];   // L row-major (even stride: 16-byte pair reads)
+  __shared__ double Lc[NB][NB];       // Lc[j][l] = L[l][j]
   __shared__ double rinv[NB];
   const int i = threadIdx.x;
   const int64_t k0 = k * NB;
@@ -77,29 +94,22 @@ __global__ __launch_bounds__(NB) void diag_block(double* __restrict__ A, int64_t
   bool notpd = false;
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
-    // lane j publishes its pivot; every lane reads it back
-    if (i == j) {
-      const double p = a[j];
-      notpd = !(p > tol) || !__builtin_isfinite(p);
-      const double r = 1.0 / sqrt(p > 0.0 ? p : 0.0);
-      rinv[j] = r;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    const double r = rinv[j];
-    const double lij = (i > j) ? a[j] * r : ((i == j) ? a[j] * r : 0.0);
+    const double p = readlane_f64(a[j], j);          // the pivot, uniform
+    if (i == j) notpd = !(p > tol) || !__builtin_isfinite(p);
+    const double r = rsqrt_f64(p > 0.0 ? p : 0.0);
+    if (i == 0) rinv[j] = r;
+    const double lij = (i >= j) ? a[j] * r : 0.0;
     a[j] = lij;
     Ls[i][j] = lij;
+    Lc[j][i] = lij;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    // a[i][l] -= L[i][j] L[l][j] for j < l <= i
+    // a[i][l] -= L[i][j] L[l][j] for l > j.  Unguarded: lanes i < j have lij = 0, and the
+    // entries l > i it writes lie above the diagonal, which are never read as pivots or
+    // column entries (a[j] of lane i < j is replaced by lij = 0) nor stored.
 #pragma unroll
-    for (int l = j + 1; l < NB; ++l) {
-      const double llj = Ls[l][j];
-      if (i >= l) a[l] = fma(-lij, llj, a[l]);
-    }
+    for (int l = j + 1; l < NB; ++l) a[l] = fma(-lij, Lc[j][l], a[l]);
   }
   if (notpd) atomicOr(flag, FLAG_NOTPD);
 #pragma unroll
@@ -110,10 +120,10 @@ __global__ __launch_bounds__(NB) void diag_block(double* __restrict__ A, int64_t
   double x[NB];
 #pragma unroll
   for (int r = 0; r < NB; ++r) {
-    double acc = (r == i) ? 1.0 : 0.0;
+    double acc[4] = {(r == i) ? 1.0 : 0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int q = 0; q < r; ++q) acc = fma(-Ls[r][q], x[q], acc);
-    x[r] = acc * rinv[r];
+    for (int q = 0; q < r; ++q) acc[q & 3] = fma(-Ls[r][q], x[q], acc[q & 3]);
+    x[r] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) * rinv[r];
   }
   double* __restrict__ out = Dinv + k * NB * NB;
 #pragma unroll
