@@ -60,8 +60,10 @@ __device__ __forceinline__ void tile_coords(int64_t pid, int64_t tm_n, int64_t t
   tn = in / gsz;
 }
 
+// Two workgroups per CU, except for EPI_SUB, whose accumulators are loaded from C up
+// front (one workgroup per CU, so the registers fit without spilling).
 template <int EPI, bool VEC>
-__global__ __launch_bounds__(kThreads, 2) void gemm_nt_kernel(const GemmArgs g) {
+__global__ __launch_bounds__(kThreads, EPI == EPI_SUB ? 1 : 2) void gemm_nt_kernel(const GemmArgs g) {
   __shared__ __attribute__((aligned(16))) float As[BM * LDK];
   __shared__ __attribute__((aligned(16))) float Bs[BN * LDK];
 
@@ -82,12 +84,30 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_nt_kernel(const GemmArgs g) 
   const bool interior = VEC && (m0 + BM <= g.M) && (n0 + BN <= g.N) && (g.K % BK == 0);
 
   f32x16 acc[2][2];
+  if constexpr (EPI == EPI_SUB) {
+    // C -= A B is computed as C + (-A) B with C loaded into the accumulators before the
+    // K loop (its latency overlaps the first slab; the epilogue is a plain store).
+    // Accumulator layout: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column
+    // l%32 of the 32 x 32 block.
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int nt = 0; nt < 2; ++nt) {
+        const int64_t col = n0 + wn * 64 + nt * 32 + (lane & 31);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = m0 + wm * 64 + mt * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          acc[mt][nt][r] = (row < g.M && col < g.N) ? g.C[row * g.ldc + col] : 0.f;
+        }
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  }
 
   // thread's chunks: chunk f = tid + 256 i -> row f / 16, float4 column f % 16
   const int crow = tid >> 4, ccol = 4 * (tid & 15);
@@ -114,7 +134,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_nt_kernel(const GemmArgs g) 
   auto sstore = [&]() {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      *reinterpret_cast<float4*>(&As[(crow + 16 * i) * LDK + ccol]) = ra[i];
+      float4 va = ra[i];
+      if constexpr (EPI == EPI_SUB) va = make_float4(-va.x, -va.y, -va.z, -va.w);
+      *reinterpret_cast<float4*>(&As[(crow + 16 * i) * LDK + ccol]) = va;
       *reinterpret_cast<float4*>(&Bs[(crow + 16 * i) * LDK + ccol]) = rb[i];
     }
   };
@@ -196,8 +218,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_nt_kernel(const GemmArgs g) 
         if (row >= g.M) continue;
         const float v = acc[mt][nt][r];
         float* c = g.C + row * g.ldc + col;
-        if (EPI == EPI_STORE) *c = v;
-        else if (EPI == EPI_SUB) *c = *c - v;
+        if (EPI == EPI_STORE || EPI == EPI_SUB) *c = v;   // EPI_SUB: acc started from C
         else if (EPI == EPI_ADD) *c = *c + v;
         else if (EPI == EPI_COLSCALE) *c = v * cv;
         else *c = (g.P[row * g.ldp + col] + g.rho * v) * inv;

@@ -150,7 +150,7 @@ int launch_check_perm(const int32_t* perm, int64_t d, uint32_t* counts, uint32_t
 // fp32 matrix-core GEMM  C (epilogue)= A[M x K] * B[N x K]^T  (k_gemm.hip)
 enum GemmEpi : int {
   EPI_STORE = 0,     // C = acc
-  EPI_SUB = 1,       // C = C - acc
+  EPI_SUB = 1,       // C = C - A B (accumulated from C with A negated)
   EPI_COLSCALE = 2,  // C = acc * colv[n]
   EPI_ADMM1 = 3,     // C = (P + rho * acc) / (colv[n] + rho)
   EPI_ADD = 4,       // C = C + acc
