@@ -10,15 +10,18 @@
 // Both operands are read K-contiguous ("NT" form), which is how every caller stores
 // them, so tiles stage straight into LDS without a transpose.  Tiles of 128 x 128 per
 // 256-thread workgroup, 4 wavefronts each owning 64 x 64 = 2 x 2 blocks of
-// v_mfma_f32_32x32x2_f32.  K advances 64 at a time: the next 64-deep slab of both
-// operands is prefetched into registers (16 x 16 B per thread) while the matrix cores
-// work through the current slab in LDS (128 MFMAs of 64 cycles per wavefront between
-// barriers), then written to the single, row-padded LDS buffer.  Two workgroups fit
-// per CU (70 KB of LDS each), so one workgroup's barrier phase is covered by the
-// other's MFMAs.  The K index within an 8-wide group is split k = 4 * (lane / 32) + e
-// between the two lane halves, identically for A and B, so each lane reads one 16-byte
-// vector per operand and feeds four MFMAs.  Interior tiles (whole tile and every slab
-// inside the matrices) use unchecked vector loads; edge tiles check every element.
+// v_mfma_f32_32x32x2_f32.  K advances 32 at a time: the next 32-deep slab of both
+// operands is prefetched into registers (4 x 16 B per operand per lane) while the
+// matrix cores work through the current slab in LDS (64 MFMAs of 64 cycles per
+// wavefront between barriers), then written to the single, row-padded LDS buffer.
+// Three workgroups share a CU (36 KB of LDS and at most 170 registers each): one
+// wavefront cannot keep a SIMD's matrix core busy on its own, so while one of the three
+// wavefronts on a SIMD is in its barrier and LDS-store phase the other two keep it at
+// full rate.  One 8-deep step's operands are live at a time (bounds the registers).
+// The K index within an 8-wide group is split k = 4 * (lane / 32) + e between the two
+// lane halves, identically for A and B, so each lane reads one 16-byte vector per
+// operand and feeds four MFMAs.  Interior tiles (whole tile and every slab inside the
+// matrices) use unchecked vector loads; edge tiles check every element.
 #include "qz_internal.h"
 
 namespace qz {
@@ -27,10 +30,10 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int BM = 128, BN = 128, BK = 32;
 constexpr int LDK = BK + 4;  // padded LDS row (floats): rows 4 banks apart
 constexpr int kThreads = 256;
-constexpr int PER = (BM * BK / 4) / kThreads;   // float4 chunks per operand per thread (8)
+constexpr int PER = (BM * BK / 4) / kThreads;   // float4 chunks per operand per thread (4)
 
 __device__ __forceinline__ float4 load4_checked(const float* __restrict__ base, int64_t row,
                                                 int64_t nrows, int64_t ld, int64_t k, int64_t K,
@@ -60,10 +63,10 @@ __device__ __forceinline__ void tile_coords(int64_t pid, int64_t tm_n, int64_t t
   tn = in / gsz;
 }
 
-// Two workgroups per CU, except for EPI_SUB, whose accumulators are loaded from C up
+// Three workgroups per CU, except for EPI_SUB, whose accumulators are loaded from C up
 // front (one workgroup per CU, so the registers fit without spilling).
 template <int EPI, bool VEC>
-__global__ __launch_bounds__(kThreads, EPI == EPI_SUB ? 1 : 2) void gemm_nt_kernel(const GemmArgs g) {
+__global__ __launch_bounds__(kThreads, EPI == EPI_SUB ? 1 : 3) void gemm_nt_kernel(const GemmArgs g) {
   __shared__ __attribute__((aligned(16))) float As[BM * LDK];
   __shared__ __attribute__((aligned(16))) float Bs[BN * LDK];
 
@@ -109,12 +112,12 @@ __global__ __launch_bounds__(kThreads, EPI == EPI_SUB ? 1 : 2) void gemm_nt_kern
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   }
 
-  // thread's chunks: chunk f = tid + 256 i -> row f / 16, float4 column f % 16
-  const int crow = tid >> 4, ccol = 4 * (tid & 15);
+  // thread's chunks: chunk f = tid + 256 i -> row f / 8, float4 column f % 8
+  const int crow = tid >> 3, ccol = 4 * (tid & 7);
   float4 ra[PER], rb[PER];
   const float* __restrict__ Ab = g.A + (m0 + crow) * g.lda + ccol;
   const float* __restrict__ Bb = g.B + (n0 + crow) * g.ldb + ccol;
-  const int64_t a_step = 16 * g.lda, b_step = 16 * g.ldb;
+  const int64_t a_step = 32 * g.lda, b_step = 32 * g.ldb;
 
   auto gload = [&](int64_t k0) {
     if (interior) {
@@ -126,8 +129,8 @@ __global__ __launch_bounds__(kThreads, EPI == EPI_SUB ? 1 : 2) void gemm_nt_kern
     } else {
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
-        ra[i] = load4_checked(g.A, m0 + crow + 16 * i, g.M, g.lda, k0 + ccol, g.K, VEC);
-        rb[i] = load4_checked(g.B, n0 + crow + 16 * i, g.N, g.ldb, k0 + ccol, g.K, VEC);
+        ra[i] = load4_checked(g.A, m0 + crow + 32 * i, g.M, g.lda, k0 + ccol, g.K, VEC);
+        rb[i] = load4_checked(g.B, n0 + crow + 32 * i, g.N, g.ldb, k0 + ccol, g.K, VEC);
       }
     }
   };
@@ -136,8 +139,8 @@ __global__ __launch_bounds__(kThreads, EPI == EPI_SUB ? 1 : 2) void gemm_nt_kern
     for (int i = 0; i < PER; ++i) {
       float4 va = ra[i];
       if constexpr (EPI == EPI_SUB) va = make_float4(-va.x, -va.y, -va.z, -va.w);
-      *reinterpret_cast<float4*>(&As[(crow + 16 * i) * LDK + ccol]) = va;
-      *reinterpret_cast<float4*>(&Bs[(crow + 16 * i) * LDK + ccol]) = rb[i];
+      *reinterpret_cast<float4*>(&As[(crow + 32 * i) * LDK + ccol]) = va;
+      *reinterpret_cast<float4*>(&Bs[(crow + 32 * i) * LDK + ccol]) = rb[i];
     }
   };
 
@@ -164,6 +167,7 @@ __global__ __launch_bounds__(kThreads, EPI == EPI_SUB ? 1 : 2) void gemm_nt_kern
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt)
             acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[mt][e], b[nt][e], acc[mt][nt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);   // one step's operands live at a time
     }
     if (kt + 1 < nk) {
       __syncthreads();   // every wave is done with the slab in LDS
