@@ -80,7 +80,8 @@ def parse():
     ap.add_argument("--ls-steps", type=int, default=256,
                     help="step limit of the local search run on ADMM-Q's result (outside the timed steps)")
     ap.add_argument("--sweep", action="store_true",
-                    help="one line per layer workload (1 warm-up and 1 timed step each), no CPU leg")
+                    help="one line per layer workload (1 warm-up and 1 timed step each), no CPU, "
+                         "orders or local-search legs")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain streaming kernel (y = -x over MIB MiB of fp32, 3 launches) "
                          "whose byte counts calibrate the HBM traffic counters, then exit")
@@ -141,7 +142,7 @@ def gptq_work(d_o, d_i, B):
     return trailing, inblock
 
 
-def run_workload(args, name, steps, warmup, with_cpu):
+def run_workload(args, name, steps, warmup, with_cpu, legs=True):
     """One bench line for workload `name` (inputs resident in HBM before timing)."""
     import numpy as np
     import torch
@@ -309,13 +310,15 @@ def run_workload(args, name, steps, warmup, with_cpu):
     del V, lam, sig
     line["components"]["objective"] = {"rtn": f_rtn, "gptq": f_gptq, "admmq": f_admm,
                                        "admmq_over_gptq": round(f_admm / f_gptq, 4)}
-    line["components"]["local_search"] = local_search_leg(q, H, W, ao, bits, group, f_admm,
-                                                          f_gptq, args.ls_steps)
-    line["components"]["orders"] = orders_leg(q, H, W, bits, group, B)
-    go = {"codes": gc, "scales": gs, "zeros": gz}
-    line["components"]["local_search_on_gptq"] = local_search_leg(q, H, W, go, bits, group, f_gptq,
-                                                                  f_gptq, args.ls_steps)
-    del ao, go
+    if legs:
+        line["components"]["local_search"] = local_search_leg(q, H, W, ao, bits, group, f_admm,
+                                                              f_gptq, args.ls_steps)
+        line["components"]["orders"] = orders_leg(q, H, W, bits, group, B)
+        go = {"codes": gc, "scales": gs, "zeros": gz}
+        line["components"]["local_search_on_gptq"] = local_search_leg(q, H, W, go, bits, group,
+                                                                      f_gptq, f_gptq, args.ls_steps)
+        del go
+    del ao
     if with_cpu:
         Xh = X[:16384].view(torch.int16).cpu().numpy().view(np.uint16)
         Wh = W[:args.cpu_rows].view(torch.int16).cpu().numpy().view(np.uint16)
@@ -398,9 +401,10 @@ def main():
         copy_probe(args.copy_probe)
         return
     if args.sweep:
-        # one line per layer workload (the tiny layer excluded), one timed step each
+        # one line per layer workload (the tiny layer excluded), one timed step each; the
+        # orders and local-search legs run on the headline line only
         for name in SWEEP:
-            line = run_workload(args, name, 1, 1, False)
+            line = run_workload(args, name, 1, 1, False, legs=False)
             line["sweep"] = True
             print(json.dumps(line), flush=True)
         return

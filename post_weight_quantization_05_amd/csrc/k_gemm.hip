@@ -10,18 +10,18 @@
 // Both operands are read K-contiguous ("NT" form), which is how every caller stores
 // them, so tiles stage straight into LDS without a transpose.  Tiles of 128 x 128 per
 // 256-thread workgroup, 4 wavefronts each owning 64 x 64 = 2 x 2 blocks of
-// v_mfma_f32_32x32x2_f32.  K advances 32 at a time: the next 32-deep slab of both
-// operands is prefetched into registers (4 x 16 B per operand per lane) while the
-// matrix cores work through the current slab in LDS (64 MFMAs of 64 cycles per
-// wavefront between barriers), then written to the single, row-padded LDS buffer.
-// Three workgroups share a CU (36 KB of LDS and at most 170 registers each): one
-// wavefront cannot keep a SIMD's matrix core busy on its own, so while one of the three
-// wavefronts on a SIMD is in its barrier and LDS-store phase the other two keep it at
-// full rate.  One 8-deep step's operands are live at a time (bounds the registers).
-// The K index within an 8-wide group is split k = 4 * (lane / 32) + e between the two
-// lane halves, identically for A and B, so each lane reads one 16-byte vector per
-// operand and feeds four MFMAs.  Interior tiles (whole tile and every slab inside the
-// matrices) use unchecked vector loads; edge tiles check every element.
+// v_mfma_f32_32x32x2_f32.  K advances one slab at a time: the next slab of both operands
+// is prefetched into registers while the matrix cores work through the current slab in
+// LDS, then written to the single, row-padded LDS buffer between two barriers.  One
+// wavefront cannot keep a SIMD's matrix core busy on its own, so co-resident workgroups
+// cover each other's barrier and LDS-store phases.  Two slab depths: 64 (70 KB of LDS,
+// two workgroups per CU, 128 MFMAs per wavefront per slab) and 32 (36 KB, three
+// workgroups per CU, so two wavefronts keep a SIMD at full rate while the third stores;
+// one 8-deep step's operands live at a time to fit the registers); the launcher picks
+// per shape.  The K index within an 8-wide group is split k = 4 * (lane / 32) + e
+// between the two lane halves, identically for A and B, so each lane reads one 16-byte
+// vector per operand and feeds four MFMAs.  Interior tiles (whole tile and every slab
+// inside the matrices) use unchecked vector loads; edge tiles check every element.
 #include "qz_internal.h"
 
 namespace qz {
@@ -30,10 +30,8 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128, BN = 128, BK = 32;
-constexpr int LDK = BK + 4;  // padded LDS row (floats): rows 4 banks apart
+constexpr int BM = 128, BN = 128;
 constexpr int kThreads = 256;
-constexpr int PER = (BM * BK / 4) / kThreads;   // float4 chunks per operand per thread (4)
 
 __device__ __forceinline__ float4 load4_checked(const float* __restrict__ base, int64_t row,
                                                 int64_t nrows, int64_t ld, int64_t k, int64_t K,
@@ -63,10 +61,17 @@ __device__ __forceinline__ void tile_coords(int64_t pid, int64_t tm_n, int64_t t
   tn = in / gsz;
 }
 
-// Three workgroups per CU, except for EPI_SUB, whose accumulators are loaded from C up
-// front (one workgroup per CU, so the registers fit without spilling).
-template <int EPI, bool VEC>
-__global__ __launch_bounds__(kThreads, EPI == EPI_SUB ? 1 : 3) void gemm_nt_kernel(const GemmArgs g) {
+// KB = slab depth: 32 (three workgroups per CU) or 64 (two per CU).  EPI_SUB, whose
+// accumulators are loaded from C up front, runs one workgroup per CU so the registers fit
+// without spilling.
+template <int EPI, bool VEC, int KB>
+__global__ __launch_bounds__(kThreads, EPI == EPI_SUB ? 1 : (KB == 32 ? 3 : 2)) void gemm_nt_kernel(
+    const GemmArgs g) {
+  constexpr int BK = KB;
+  constexpr int LDK = BK + 4;                       // padded LDS row (floats): rows 4 banks apart
+  constexpr int PER = (BM * BK / 4) / kThreads;     // float4 chunks per operand per thread
+  constexpr int CPR = BK / 4;                       // float4 chunks per row
+  constexpr int RSTEP = kThreads / CPR;             // rows between a thread's chunks
   __shared__ __attribute__((aligned(16))) float As[BM * LDK];
   __shared__ __attribute__((aligned(16))) float Bs[BN * LDK];
 
@@ -112,12 +117,12 @@ __global__ __launch_bounds__(kThreads, EPI == EPI_SUB ? 1 : 3) void gemm_nt_kern
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   }
 
-  // thread's chunks: chunk f = tid + 256 i -> row f / 8, float4 column f % 8
-  const int crow = tid >> 3, ccol = 4 * (tid & 7);
+  // thread's chunks: chunk f = tid + 256 i -> row f / CPR, float4 column f % CPR
+  const int crow = tid / CPR, ccol = 4 * (tid % CPR);
   float4 ra[PER], rb[PER];
   const float* __restrict__ Ab = g.A + (m0 + crow) * g.lda + ccol;
   const float* __restrict__ Bb = g.B + (n0 + crow) * g.ldb + ccol;
-  const int64_t a_step = 32 * g.lda, b_step = 32 * g.ldb;
+  const int64_t a_step = RSTEP * g.lda, b_step = RSTEP * g.ldb;
 
   auto gload = [&](int64_t k0) {
     if (interior) {
@@ -129,8 +134,8 @@ __global__ __launch_bounds__(kThreads, EPI == EPI_SUB ? 1 : 3) void gemm_nt_kern
     } else {
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
-        ra[i] = load4_checked(g.A, m0 + crow + 32 * i, g.M, g.lda, k0 + ccol, g.K, VEC);
-        rb[i] = load4_checked(g.B, n0 + crow + 32 * i, g.N, g.ldb, k0 + ccol, g.K, VEC);
+        ra[i] = load4_checked(g.A, m0 + crow + RSTEP * i, g.M, g.lda, k0 + ccol, g.K, VEC);
+        rb[i] = load4_checked(g.B, n0 + crow + RSTEP * i, g.N, g.ldb, k0 + ccol, g.K, VEC);
       }
     }
   };
@@ -139,8 +144,8 @@ __global__ __launch_bounds__(kThreads, EPI == EPI_SUB ? 1 : 3) void gemm_nt_kern
     for (int i = 0; i < PER; ++i) {
       float4 va = ra[i];
       if constexpr (EPI == EPI_SUB) va = make_float4(-va.x, -va.y, -va.z, -va.w);
-      *reinterpret_cast<float4*>(&As[(crow + 32 * i) * LDK + ccol]) = va;
-      *reinterpret_cast<float4*>(&Bs[(crow + 32 * i) * LDK + ccol]) = rb[i];
+      *reinterpret_cast<float4*>(&As[(crow + RSTEP * i) * LDK + ccol]) = va;
+      *reinterpret_cast<float4*>(&Bs[(crow + RSTEP * i) * LDK + ccol]) = rb[i];
     }
   };
 
@@ -167,7 +172,8 @@ __global__ __launch_bounds__(kThreads, EPI == EPI_SUB ? 1 : 3) void gemm_nt_kern
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt)
             acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[mt][e], b[nt][e], acc[mt][nt], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);   // one step's operands live at a time
+      // at three workgroups per CU, one step's operands live at a time (bounds registers)
+      if constexpr (KB == 32) __builtin_amdgcn_sched_barrier(0);
     }
     if (kt + 1 < nk) {
       __syncthreads();   // every wave is done with the slab in LDS
@@ -231,6 +237,25 @@ __global__ __launch_bounds__(kThreads, EPI == EPI_SUB ? 1 : 3) void gemm_nt_kern
   }
 }
 
+// Slab depth per launch: 32-deep slabs with three workgroups per CU keep the matrix cores
+// busier, but they pay when the tiles do not fill whole rounds of 768 resident
+// workgroups (the last round runs part-empty) and, as measured, for long K (12288 and
+// 25600 ran slower than with 64-deep slabs); 64-deep slabs with two workgroups per CU
+// are used otherwise.  EPI_SUB (the short-K GPTQ update) uses 64.
+inline int slab_depth(int epi, int64_t tiles, int64_t K) {
+  if (epi == EPI_SUB) return 64;
+  return (tiles % (3 * 256) == 0 && K <= 8192) ? 32 : 64;
+}
+
+template <int EPI, int KB>
+int launch_kb(const GemmArgs& a, int64_t tiles, bool vec, hipStream_t s) {
+  if (vec)
+    gemm_nt_kernel<EPI, true, KB><<<static_cast<unsigned>(tiles), kThreads, 0, s>>>(a);
+  else
+    gemm_nt_kernel<EPI, false, KB><<<static_cast<unsigned>(tiles), kThreads, 0, s>>>(a);
+  return check_launch("gemm_nt");
+}
+
 template <int EPI>
 int launch_epi(const GemmArgs& a, hipStream_t s) {
   const int64_t tiles = ceil_div(a.M, BM) * ceil_div(a.N, BN);
@@ -238,11 +263,8 @@ int launch_epi(const GemmArgs& a, hipStream_t s) {
   const bool vec = (a.lda % 4 == 0) && (a.ldb % 4 == 0) &&
                    (reinterpret_cast<uintptr_t>(a.A) % 16 == 0) &&
                    (reinterpret_cast<uintptr_t>(a.B) % 16 == 0);
-  if (vec)
-    gemm_nt_kernel<EPI, true><<<static_cast<unsigned>(tiles), kThreads, 0, s>>>(a);
-  else
-    gemm_nt_kernel<EPI, false><<<static_cast<unsigned>(tiles), kThreads, 0, s>>>(a);
-  return check_launch("gemm_nt");
+  if (slab_depth(EPI, tiles, a.K) == 32) return launch_kb<EPI, 32>(a, tiles, vec, s);
+  return launch_kb<EPI, 64>(a, tiles, vec, s);
 }
 
 }  // namespace
