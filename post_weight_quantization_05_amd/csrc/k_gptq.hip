@@ -9,10 +9,13 @@
 // 128-column block never leaves the register file.  At step j the owner lane of the
 // column rounds it (IEEE fp32 division, half-to-even), forms E, and a DPP quad
 // broadcast hands E to the other three lanes; each lane then updates its remaining
-// columns with R[j, :] read from LDS (stored lane-deinterleaved so one quad reads 4
-// distinct 16-byte vectors, broadcast across the 16 quads of the wavefront).
-// The trailing update of the columns after the block is the separate matrix-core
-// GEMM (k_gemm.hip).
+// columns with R[j, :] read from LDS (stored lane-deinterleaved and padded, so the
+// four distinct slices a wavefront reads per instruction, and the staging writes, are
+// free of bank conflicts).  The workgroup's set-up stages R's block and each row's
+// (scale, zero) per column with many global loads in flight (clamped addresses, selected
+// afterwards); at the end E leaves through LDS as whole rows and, in natural order, the
+// codes as 16-byte row pieces.  The trailing update of the columns after the block is
+// the separate matrix-core GEMM (k_gemm.hip).
 #include "qz_internal.h"
 
 namespace qz {
@@ -23,6 +26,8 @@ constexpr int MAXB = 128;        // largest block
 constexpr int ROWS = 64;         // rows per workgroup
 constexpr int kThreads = 256;    // 4 lanes per row
 constexpr int PER = MAXB / 4;    // columns per lane
+constexpr int RQ = PER + 1;      // LDS stride of the four lane slices of an R row
+constexpr int RJ = 4 * RQ + 1;   // LDS stride of an R row
 
 __device__ __forceinline__ float quad_bcast(float v, int owner) {
   // DPP quad_perm with all four selectors = owner
@@ -52,10 +57,13 @@ __global__ __launch_bounds__(kThreads) void gptq_block_kernel(
     const uint8_t* __restrict__ zeros, int64_t G, int group, float maxq,
     const int32_t* __restrict__ perm, float* __restrict__ E, int64_t lde,
     uint8_t* __restrict__ codes, int32_t* __restrict__ codes32, int64_t d_i) {
-  __shared__ __attribute__((aligned(16))) float Rb[MAXB][4][PER];   // Rb[j][q][i] = R[a+j][a+q+4i]
-  __shared__ __attribute__((aligned(8))) float2 sz[ROWS][MAXB];      // (scale, zero) of (row, column)
+  // R[a+j][a+q+4i] at Rb[j * RJ + q * RQ + i]: q stride 33 and j stride 133 (5 mod 64
+  // banks), so the staging writes (consecutive j across lanes) and the step reads (four
+  // q per instruction) are free of bank conflicts
+  __shared__ __attribute__((aligned(16))) float Rb[MAXB * RJ];
+  __shared__ __attribute__((aligned(16))) float2 sz[ROWS][MAXB];     // (scale, zero) of (row, column)
   __shared__ float rinv[MAXB];
-  __shared__ uint8_t cs[ROWS][MAXB];
+  __shared__ __attribute__((aligned(16))) uint8_t cs[ROWS][MAXB];
 
   const int tid = threadIdx.x;
   const int q = tid & 3;
@@ -64,24 +72,59 @@ __global__ __launch_bounds__(kThreads) void gptq_block_kernel(
   const int64_t row = row0 + rl;
   const bool rok = row < d_o;
 
-  // R block (upper part, c >= j) into LDS, deinterleaved by lane.
-  for (int e = tid; e < MAXB * MAXB; e += kThreads) {
-    const int c = e / MAXB, j = e % MAXB;   // j fastest: contiguous reads of Rt row a+c
-    float v = 0.f;
-    if (c < w && j < w && c >= j) v = Rt[(a + c) * ldr + a + j];
-    Rb[j][c & 3][c >> 2] = v;
+  // R block (upper part, c >= j) into LDS, deinterleaved by lane.  Loads are issued 16 at
+  // a time from clamped (always valid) addresses and selected afterwards, so their
+  // latencies overlap.
+  {
+    constexpr int RIT = MAXB * MAXB / kThreads;
+    constexpr int RU = 16;
+#pragma unroll
+    for (int it0 = 0; it0 < RIT; it0 += RU) {
+      float v[RU];
+#pragma unroll
+      for (int u = 0; u < RU; ++u) {
+        const int e = tid + (it0 + u) * kThreads;
+        const int c = e / MAXB, j = e % MAXB;   // j fastest: contiguous reads of Rt row a+c
+        const int cc = c < w ? c : w - 1, jj = j < w ? j : w - 1;
+        const float x = Rt[(a + cc) * ldr + a + jj];
+        v[u] = (c < w && j < w && c >= j) ? x : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < RU; ++u) {
+        const int e = tid + (it0 + u) * kThreads;
+        const int c = e / MAXB, j = e % MAXB;
+        Rb[j * RJ + (c & 3) * RQ + (c >> 2)] = v[u];
+      }
+    }
   }
   for (int j = tid; j < w; j += kThreads) rinv[j] = 1.0f / Rt[(a + j) * ldr + a + j];
-  // each row's grid for each block column (groups are ranges of ORIGINAL columns)
-  for (int e = tid; e < ROWS * w; e += kThreads) {
-    const int r = e / w, c = e % w;
-    float2 v = make_float2(1.f, 0.f);
-    if (row0 + r < d_o) {
-      const int64_t oc = perm ? perm[a + c] : a + c;
-      const int64_t gi = (row0 + r) * G + oc / group;
-      v = make_float2(scales[gi], static_cast<float>(zeros[gi]));
+  // each row's grid for each block column (groups are ranges of ORIGINAL columns), 8
+  // (row, column) pairs per thread at a time from clamped addresses
+  {
+    constexpr int GIT = ROWS * MAXB / kThreads;
+    constexpr int GU = 16;
+    const int64_t last_row = d_o - 1;
+#pragma unroll
+    for (int it0 = 0; it0 < GIT; it0 += GU) {
+      float sv[GU], zv[GU];
+#pragma unroll
+      for (int u = 0; u < GU; ++u) {
+        const int e = tid + (it0 + u) * kThreads;
+        const int r = e / MAXB, c = e % MAXB;
+        const int cc = c < w ? c : w - 1;
+        const int64_t rr = (row0 + r) < last_row ? (row0 + r) : last_row;
+        const int64_t oc = perm ? perm[a + cc] : a + cc;
+        const int64_t gi = rr * G + oc / group;
+        sv[u] = scales[gi];
+        zv[u] = static_cast<float>(zeros[gi]);
+      }
+#pragma unroll
+      for (int u = 0; u < GU; ++u) {
+        const int e = tid + (it0 + u) * kThreads;
+        const int r = e / MAXB, c = e % MAXB;
+        sz[r][c] = (row0 + r < d_o) ? make_float2(sv[u], zv[u]) : make_float2(1.f, 0.f);
+      }
     }
-    sz[r][c] = v;
   }
 
   float wr[PER];
@@ -112,7 +155,7 @@ __global__ __launch_bounds__(kThreads) void gptq_block_kernel(
         cs[rl][j] = static_cast<uint8_t>(c);
     }
     const float e = quad_bcast(err, owner);
-    const float* rrow = &Rb[j][q][0];
+    const float* rrow = &Rb[j * RJ + q * RQ];
 #pragma unroll
     for (int i = slot; i < PER; ++i) {
       const int col = q + 4 * i;
@@ -124,13 +167,33 @@ __global__ __launch_bounds__(kThreads) void gptq_block_kernel(
   }
   __syncthreads();
 
-  if (rok) {
+  // E goes out through LDS (the grid's area is free after the loop) so that each
+  // wavefront writes whole rows; rows of Es are 132 floats apart (conflict-free writes)
+  {
+    constexpr int ES = MAXB + 4;
+    float* Es = reinterpret_cast<float*>(&sz[0][0]);
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int c = q + 4 * i;
-      if (c < w) E[row * lde + c] = wr[i];
+    for (int i = 0; i < PER; ++i) Es[rl * ES + q + 4 * i] = wr[i];
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < (ROWS * MAXB / 4) / kThreads; ++u) {
+      const int k = tid + u * kThreads;
+      const int r = k / (MAXB / 4), c4 = 4 * (k % (MAXB / 4));
+      const int64_t grow = row0 + r;
+      if (grow >= d_o || c4 >= w) continue;
+      const float4 v = *reinterpret_cast<const float4*>(&Es[r * ES + c4]);
+      float* dst = E + grow * lde + c4;
+      if (c4 + 3 < w) {
+        *reinterpret_cast<float4*>(dst) = v;
+      } else {
+        dst[0] = v.x;
+        if (c4 + 1 < w) dst[1] = v.y;
+        if (c4 + 2 < w) dst[2] = v.z;
+      }
     }
-    if constexpr (NOCLIP) {
+  }
+  if constexpr (NOCLIP) {
+    if (rok) {
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
         const int c = q + 4 * i;
@@ -138,11 +201,23 @@ __global__ __launch_bounds__(kThreads) void gptq_block_kernel(
         const int64_t oc = perm ? perm[a + c] : a + c;
         codes32[row * d_i + oc] = static_cast<int32_t>(cr[i]);
       }
-    } else {
-      for (int c = q; c < w; c += 4) {
-        const int64_t oc = perm ? perm[a + c] : a + c;
-        codes[row * d_i + oc] = cs[rl][c];
-      }
+    }
+  } else if (!perm && w == MAXB && (d_i % 16) == 0 &&
+             (reinterpret_cast<uintptr_t>(codes) & 15) == 0) {
+    // natural order, full block: each row's 128 codes are contiguous, 16 bytes per store
+#pragma unroll
+    for (int u = 0; u < (ROWS * MAXB / 16) / kThreads; ++u) {
+      const int k = tid + u * kThreads;
+      const int r = k / (MAXB / 16), c16 = 16 * (k % (MAXB / 16));
+      const int64_t grow = row0 + r;
+      if (grow >= d_o) continue;
+      *reinterpret_cast<uint4*>(codes + grow * d_i + a + c16) =
+          *reinterpret_cast<const uint4*>(&cs[r][c16]);
+    }
+  } else if (rok) {
+    for (int c = q; c < w; c += 4) {
+      const int64_t oc = perm ? perm[a + c] : a + c;
+      codes[row * d_i + oc] = cs[rl][c];
     }
   }
 }
