@@ -76,6 +76,21 @@ def test_objective_full_layer():
     assert abs(f - ref) <= TOL * ref
 
 
+def test_objective_ragged_shape_with_32_deep_slabs():
+    """A shape whose product has exactly 768 tiles (96 x 8) with ragged M, N and K
+    (12285 x 1019 x 1019), so the matrix-core product runs its 32-deep, three-workgroup
+    configuration on edge tiles with element-checked loads; rows against the oracle."""
+    q = qz()
+    d_o, d_i = 12285, 1019
+    Hf, W, Wd, codes, s, z = _case(5, d_o, d_i, d_i, 3, True)
+    f, rows = q.qz_objective(to_dev(Hf), Wd, to_dev(codes), to_dev(s), to_dev(z), d_i, rows=True)
+    H64 = Hf.astype(np.float64)
+    ref_rows = objective.row_objective(H64, W, grid.dequant(codes, s, z, d_i))
+    report("objective_ragged768", rel=abs(f - ref_rows.sum()) / ref_rows.sum())
+    np.testing.assert_allclose(to_host(rows), ref_rows, rtol=TOL, atol=TOL * ref_rows.mean())
+    assert abs(f - ref_rows.sum()) <= TOL * ref_rows.sum()
+
+
 def test_objective_nonfinite_weight_is_reported():
     q = qz()
     Hf, W, Wd, codes, s, z = _case(5, 16, 64, 32, 4, False)
