@@ -76,7 +76,7 @@ size_t gptq_ws(int64_t d_o, int64_t d_i) {
   Carver c(nullptr);
   c.take<uint32_t>(1);
   c.take<float>(static_cast<size_t>(d_o) * round_up(d_i, 4));   // W working copy
-  c.take<float>(static_cast<size_t>(d_o) * 128);                 // E
+  c.take<float>(static_cast<size_t>(d_o) * 512);                 // E of a super-block
   c.take<float>(static_cast<size_t>(d_i) * round_up(d_i, 4));   // R^T
   c.take<uint32_t>(static_cast<size_t>(d_i));                    // permutation check
   c.used += rfactor_ws_bytes(d_i);
@@ -193,7 +193,14 @@ static int gptq_run(const float* H, const void* W_hat, int32_t wt, int64_t d_o, 
     return fail(QZ_EWORKSPACE, "gptq: workspace must be 256-byte aligned");
   set_error("");
 
-  const int64_t ldw = round_up(d_i, 4), lde = 128, ldr = round_up(d_i, 4);
+  // Two levels of lazy updates: blocks of B columns are grouped in super-blocks of up to
+  // 512 columns; a block's E updates only the rest of its super-block, and after the
+  // super-block one product with K = its width updates every later column (the same sums
+  // as one update per block, in exact arithmetic, with far fewer passes over W).  A
+  // block's E columns start 16-byte aligned inside the super-block's E only when B is a
+  // multiple of 4; otherwise a super-block is one block.
+  const int64_t SB = (B % 4 == 0) ? 512 / B : 1;   // blocks per super-block
+  const int64_t ldw = round_up(d_i, 4), lde = 512, ldr = round_up(d_i, 4);
   const int64_t G = d_i / grid->group_size;
   Carver cv(ws);
   uint32_t* flag = cv.take<uint32_t>(1);
@@ -228,27 +235,35 @@ static int gptq_run(const float* H, const void* W_hat, int32_t wt, int64_t d_o, 
   if (h & FLAG_NOTPD) return fail(QZ_ENOTPD, "gptq: H is not positive definite (increase damping)");
   if (d_o == 0) return QZ_OK;
 
-  for (int64_t a = 0; a < d_i; a += B) {
-    const int64_t b = (a + B < d_i) ? a + B : d_i;
-    {
-      ScopedTimer tm(K_GPTQ_BLOCK, stream);
-      QZ_TRY(launch_gptq_block(Wf, ldw, d_o, a, b, Rt, ldr, scales, zeros, G, grid->group_size,
-                               grid->bits, perm, E, lde, codes, codes32, d_i, stream));
+  auto update = [&](const float* Eop, int64_t K, int64_t col0, int64_t ncols, int64_t rk) {
+    // W[:, col0 : col0 + ncols] -= Eop[:, 0:K] R[rk : rk + K, col0 : col0 + ncols]
+    GemmArgs g{};
+    g.M = d_o;
+    g.N = ncols;
+    g.K = K;
+    g.A = Eop;
+    g.lda = lde;
+    g.B = Rt + col0 * ldr + rk;   // row col0+n, columns rk.. : R[rk+k][col0+n]
+    g.ldb = ldr;
+    g.C = Wf + col0;
+    g.ldc = ldw;
+    ScopedTimer tm(K_GEMM_GPTQ, stream);
+    return launch_gemm_nt(EPI_SUB, g, stream);
+  };
+  for (int64_t A = 0; A < d_i; A += SB * B) {
+    const int64_t Aend = (A + SB * B < d_i) ? A + SB * B : d_i;
+    for (int64_t a = A; a < Aend; a += B) {
+      const int64_t b = (a + B < Aend) ? a + B : Aend;
+      float* Eb = E + (a - A);
+      {
+        ScopedTimer tm(K_GPTQ_BLOCK, stream);
+        QZ_TRY(launch_gptq_block(Wf, ldw, d_o, a, b, Rt, ldr, scales, zeros, G,
+                                 grid->group_size, grid->bits, perm, Eb, lde, codes, codes32, d_i,
+                                 stream));
+      }
+      if (b < Aend) QZ_TRY(update(Eb, b - a, b, Aend - b, a));          // rest of the super-block
     }
-    if (b < d_i) {
-      GemmArgs g{};
-      g.M = d_o;
-      g.N = d_i - b;
-      g.K = b - a;
-      g.A = E;
-      g.lda = lde;
-      g.B = Rt + b * ldr + a;   // row b+n, columns a.. : R[a+k][b+n]
-      g.ldb = ldr;
-      g.C = Wf + b;
-      g.ldc = ldw;
-      ScopedTimer tm(K_GEMM_GPTQ, stream);
-      QZ_TRY(launch_gemm_nt(EPI_SUB, g, stream));
-    }
+    if (Aend < d_i) QZ_TRY(update(E, Aend - A, Aend, d_i - Aend, A));   // every later column
   }
   return QZ_OK;
 }

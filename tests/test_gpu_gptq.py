@@ -85,7 +85,8 @@ def test_gptq_tiny_layer():
 
 @pytest.mark.parametrize("d_o,d_i,bits,group,B", [(70, 200, 3, 8, 48), (64, 128, 2, 128, 1),
                                                    (64, 128, 3, 128, 128), (33, 384, 3, 128, 128),
-                                                   (130, 256, 4, 1, 37), (5, 40, 8, 40, 16)])
+                                                   (130, 256, 4, 1, 37), (5, 40, 8, 40, 16),
+                                                   (40, 1100, 3, 100, 40)])
 def test_gptq_ragged(d_o, d_i, bits, group, B):
     X = qz_synth.calib_bf16(9, 4 * d_i, d_i, p_out=0.02, f_out=30.0)
     H, _ = hessian.hessian(X, 0.01)
