@@ -18,6 +18,8 @@
 // the not-positive-definite flag; the caller reads it at its sync point (the GPTQ
 // tutorial's damping section: a failed factorisation means more damping is needed).
 // Output: R^T (lower, row-major) in fp32, the layout the GPTQ kernels read.
+#include <vector>
+
 #include "qz_internal.h"
 
 namespace qz {
@@ -202,12 +204,21 @@ __global__ __launch_bounds__(kThreads) void panel_solve(double* __restrict__ A, 
 }
 
 // Cholesky trailing update after block column k: lower tiles (ti >= tj) of the
-// trailing matrix, A[i][j] -= L[i][k-block] L[j][k-block]^T.
-__global__ __launch_bounds__(kThreads) void chol_trailing(double* __restrict__ A, int64_t lda, int64_t k) {
+// trailing matrix from block `first` on, A[i][j] -= L[i][k-block] L[j][k-block]^T.
+__global__ __launch_bounds__(kThreads) void chol_trailing(double* __restrict__ A, int64_t lda, int64_t k,
+                                                          int64_t first) {
   int64_t ti, tj;
   tri_tile(blockIdx.x, ti, tj);
-  const int64_t base = (k + 1) * NB;
+  const int64_t base = first * NB;
   const int64_t i0 = base + ti * NB, j0 = base + tj * NB, k0 = k * NB;
+  tile_update<false>(A, lda, i0, j0, A, lda, i0, k0, A, lda, k0, j0);
+}
+
+// The same update restricted to block column k + 1 (the next diagonal block's column).
+__global__ __launch_bounds__(kThreads) void chol_trailing_col(double* __restrict__ A, int64_t lda,
+                                                              int64_t k) {
+  const int64_t j0 = (k + 1) * NB;
+  const int64_t i0 = j0 + static_cast<int64_t>(blockIdx.x) * NB, k0 = k * NB;
   tile_update<false>(A, lda, i0, j0, A, lda, i0, k0, A, lda, k0, j0);
 }
 
@@ -268,23 +279,103 @@ size_t rfactor_ws_bytes(int64_t d) {
 
 namespace {
 
-// The reversed-order Cholesky in place: A (lower) = L with L L^T = J Hp J, plus the
-// inverses of the diagonal blocks in Dinv.
+// Streams and events for the look-ahead schedule, created once per host thread and
+// device (default priority; kept until the process ends).  When they cannot be created
+// every launch goes to the caller's stream.
+struct Lookahead {
+  int device = -1;
+  bool ok = false;
+  hipStream_t trail = nullptr, inv = nullptr;
+  hipEvent_t ev_panel = nullptr, ev_trail = nullptr, ev_join1 = nullptr, ev_join2 = nullptr;
+};
+
+Lookahead* lookahead() {
+  thread_local std::vector<Lookahead> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  for (Lookahead& l : cache)
+    if (l.device == dev) return l.ok ? &l : nullptr;
+  Lookahead l;
+  l.device = dev;
+  l.ok = hipStreamCreateWithFlags(&l.trail, hipStreamNonBlocking) == hipSuccess &&
+         hipStreamCreateWithFlags(&l.inv, hipStreamNonBlocking) == hipSuccess &&
+         hipEventCreateWithFlags(&l.ev_panel, hipEventDisableTiming) == hipSuccess &&
+         hipEventCreateWithFlags(&l.ev_trail, hipEventDisableTiming) == hipSuccess &&
+         hipEventCreateWithFlags(&l.ev_join1, hipEventDisableTiming) == hipSuccess &&
+         hipEventCreateWithFlags(&l.ev_join2, hipEventDisableTiming) == hipSuccess;
+  cache.push_back(l);
+  return cache.back().ok ? &cache.back() : nullptr;
+}
+
+// The reversed-order Cholesky in place, A (lower) = L with L L^T = J Hp J, plus the
+// inverses of the diagonal blocks in Dinv and, when X is given, X = L^{-1}.
+//
+// Look-ahead schedule.  The caller's stream runs the critical chain: per block column
+// k the diagonal block, the panel below it, and the trailing update of block column
+// k + 1 only (all the next diagonal block needs).  A second stream applies block column
+// k to the rest of the trailing matrix (columns >= k + 2) while the chain moves on; a
+// third runs inverse step k (X row block k and its update of the rows below) as soon as
+// the panel of k is done.  The update of column k + 1 waits for the previous step's
+// rest update, so every tile still receives its updates in order of k, and the results
+// are those of the one-stream order.
 int factor_reversed(const float* H, int64_t d, const int32_t* perm, double* A, int64_t dp,
-                    double* Dinv, double* diag0, uint32_t* flag, hipStream_t s) {
+                    double* Dinv, double* diag0, double* X, uint32_t* flag, hipStream_t s) {
   const int64_t nblk = dp / NB;
+  Lookahead* la = lookahead();
+  hipStream_t s_trail = la ? la->trail : s, s_inv = la ? la->inv : s;
+  auto fork = [&](hipStream_t to, hipEvent_t ev) -> int {
+    if (!la) return QZ_OK;
+    QZ_HIP(hipStreamWaitEvent(to, ev, 0));
+    return QZ_OK;
+  };
+  auto mark = [&](hipEvent_t ev, hipStream_t on) -> int {
+    if (!la) return QZ_OK;
+    QZ_HIP(hipEventRecord(ev, on));
+    return QZ_OK;
+  };
   init_reversed<<<grid_for(dp * dp), kThreads, 0, s>>>(H, d, perm, A, dp, diag0, flag);
   QZ_TRY(check_launch("rfactor.init"));
+  if (X) {
+    fill_identity<<<grid_for(dp * dp), kThreads, 0, s>>>(X, dp);
+    QZ_TRY(check_launch("rfactor.fill"));
+  }
   for (int64_t k = 0; k < nblk; ++k) {
+    const int64_t below = nblk - k - 1;
     diag_block<<<1, NB, 0, s>>>(A, dp, k, diag0, Dinv, flag);
     QZ_TRY(check_launch("rfactor.diag"));
-    const int64_t below = nblk - k - 1;
     if (below > 0) {
       panel_solve<<<static_cast<unsigned>(below), kThreads, 0, s>>>(A, dp, k, Dinv);
       QZ_TRY(check_launch("rfactor.panel"));
-      chol_trailing<<<static_cast<unsigned>(below * (below + 1) / 2), kThreads, 0, s>>>(A, dp, k);
+    }
+    QZ_TRY(mark(la ? la->ev_panel : nullptr, s));
+    QZ_TRY(fork(s_trail, la ? la->ev_panel : nullptr));
+    if (X) QZ_TRY(fork(s_inv, la ? la->ev_panel : nullptr));
+    if (below > 0) {
+      if (k > 0) QZ_TRY(fork(s, la ? la->ev_trail : nullptr));   // rest update of k - 1 done
+      chol_trailing_col<<<static_cast<unsigned>(below), kThreads, 0, s>>>(A, dp, k);
+      QZ_TRY(check_launch("rfactor.trailing_col"));
+    }
+    if (below > 1) {
+      chol_trailing<<<static_cast<unsigned>((below - 1) * below / 2), kThreads, 0, s_trail>>>(
+          A, dp, k, k + 2);
       QZ_TRY(check_launch("rfactor.trailing"));
     }
+    QZ_TRY(mark(la ? la->ev_trail : nullptr, s_trail));
+    if (X) {
+      inv_rowscale<<<static_cast<unsigned>(k + 1), kThreads, 0, s_inv>>>(X, dp, k, Dinv);
+      QZ_TRY(check_launch("rfactor.rowscale"));
+      if (below > 0) {
+        inv_update<<<static_cast<unsigned>(below * (k + 1)), kThreads, 0, s_inv>>>(X, dp, A, dp, k);
+        QZ_TRY(check_launch("rfactor.invupdate"));
+      }
+    }
+  }
+  // join: the caller's stream continues after both side streams
+  QZ_TRY(mark(la ? la->ev_join1 : nullptr, s_trail));
+  QZ_TRY(fork(s, la ? la->ev_join1 : nullptr));
+  if (X) {
+    QZ_TRY(mark(la ? la->ev_join2 : nullptr, s_inv));
+    QZ_TRY(fork(s, la ? la->ev_join2 : nullptr));
   }
   return QZ_OK;
 }
@@ -310,19 +401,7 @@ int rfactor(const float* H, int64_t d, const int32_t* perm, float* Rt, int64_t l
   double* X = cv.take<double>(static_cast<size_t>(dp) * dp);
   double* Dinv = cv.take<double>(static_cast<size_t>(nblk) * NB * NB);
   double* diag0 = cv.take<double>(static_cast<size_t>(dp));
-
-  QZ_TRY(factor_reversed(H, d, perm, A, dp, Dinv, diag0, flag, s));
-  fill_identity<<<grid_for(dp * dp), kThreads, 0, s>>>(X, dp);
-  QZ_TRY(check_launch("rfactor.fill"));
-  for (int64_t i = 0; i < nblk; ++i) {
-    inv_rowscale<<<static_cast<unsigned>(i + 1), kThreads, 0, s>>>(X, dp, i, Dinv);
-    QZ_TRY(check_launch("rfactor.rowscale"));
-    const int64_t below = nblk - i - 1;
-    if (below > 0) {
-      inv_update<<<static_cast<unsigned>(below * (i + 1)), kThreads, 0, s>>>(X, dp, A, dp, i);
-      QZ_TRY(check_launch("rfactor.invupdate"));
-    }
-  }
+  QZ_TRY(factor_reversed(H, d, perm, A, dp, Dinv, diag0, X, flag, s));
   extract_rt<<<grid_for(d * d), kThreads, 0, s>>>(X, dp, d, Rt, ldr);
   return check_launch("rfactor.extract");
 }
@@ -336,7 +415,7 @@ int order_pivots(const float* H, int64_t d, const int32_t* perm, double* D, void
   cv.take<double>(static_cast<size_t>(dp) * dp);   // (the inverse's buffer, unused here)
   double* Dinv = cv.take<double>(static_cast<size_t>(nblk) * NB * NB);
   double* diag0 = cv.take<double>(static_cast<size_t>(dp));
-  QZ_TRY(factor_reversed(H, d, perm, A, dp, Dinv, diag0, flag, s));
+  QZ_TRY(factor_reversed(H, d, perm, A, dp, Dinv, diag0, nullptr, flag, s));
   pivots_from_factor<<<grid_for(d), kThreads, 0, s>>>(A, dp, d, D);
   return check_launch("order_pivots");
 }
