@@ -127,8 +127,10 @@ int qz_rtn(const void* W, int32_t wt, int64_t d_o, int64_t d_i, const qz_grid* g
  * here).  Columns are processed in blocks of B in a common order for all rows
  * (`perm`, or natural order); in each block every column is rounded on its
  * row's static grid, E = (w - q) / R_jj is kept and the block's remaining
- * columns get E R[j, j:b]; after the block the trailing columns get one
- * matrix-core product update W[:, b:] -= E R[a:b, b:].
+ * columns get E R[j, j:b]; the later columns get the matrix-core product update
+ * W[:, b:] -= E R[a:b, b:], applied lazily in two levels (a block's E updates the
+ * rest of its group of up to 512 columns at once, the group's E all later columns
+ * after the group: the same sums in a different order).
  *   H      [d_i x d_i] fp32 symmetric positive definite.
  *   W_hat  [d_o x d_i] (dtype wt).
  *   B      block size, 1 .. 128.
@@ -138,9 +140,12 @@ int qz_rtn(const void* W, int32_t wt, int64_t d_o, int64_t d_i, const qz_grid* g
  *   codes  [d_o x d_i] u8 out; scales/zeros [d_o x d_i/g] out (in with
  *          QZ_GRID_CALLER).
  * R is computed in fp64 (blocked Cholesky of the reversed H, triangular
- * inverse) and used in fp32.  SYNC: returns QZ_ENOTPD when a pivot of the
- * factorisation is <= 1e-12 of its diagonal entry (or not finite), and
- * QZ_ENONFINITE for non-finite W_hat.                                       */
+ * inverse) and used in fp32; the factorisation runs part of its work on two
+ * library-owned side streams (default priority, one pair per host thread and
+ * device) that join `stream` before the call goes on, so the call still orders
+ * on `stream` only.  SYNC: returns QZ_ENOTPD when a pivot of the factorisation
+ * is <= 1e-12 of its diagonal entry (or not finite), and QZ_ENONFINITE for
+ * non-finite W_hat.                                                         */
 size_t qz_gptq_workspace(int64_t d_o, int64_t d_i, int32_t B);
 int qz_gptq(const float* H, const void* W_hat, int32_t wt, int64_t d_o, int64_t d_i,
             const qz_grid* grid, int32_t B, const int32_t* perm,
