@@ -102,33 +102,70 @@ def copy_probe(mib):
                       "launches": 3}), flush=True)
 
 
-def cpu_baseline(cfg, X, W_bits, rows, iters):
-    """The fp64 oracle on the host: ADMM-Q iterations on a sample of rows (rows are
-    independent), scaled to the whole layer; the eigendecomposition is excluded as
-    it is on the GPU.  H comes from the oracle on the same tokens."""
-    import numpy as np
-    from oracle import admm, hessian
+def _host_info():
+    """CPU model and the BLAS library NumPy runs on, with its thread count."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas, threads = "unknown", os.cpu_count()
     try:
         from threadpoolctl import threadpool_info
-        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=os.cpu_count())
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"] or threadpool_info()
+        if info:
+            blas = f"{info[0].get('internal_api', '?')} {info[0].get('version', '')}".strip()
+            threads = max(i.get("num_threads", 1) for i in info)
     except Exception:  # noqa: BLE001
-        cores = os.cpu_count()
+        pass
+    return model, blas, int(threads)
+
+
+def cpu_baseline(cfg, X, W_bits, rows, iters, gptq_rows=1024):
+    """The fp64 oracle on the host: ADMM-Q iterations on a sample of rows (rows are
+    independent), scaled to the whole layer; the eigendecomposition is excluded from
+    the value as it is on the GPU, and timed as a phase.  H comes from the oracle on the
+    same tokens.  Phases also time GPTQ's inverse factor and its column loop on a smaller
+    row sample (scaled to the layer)."""
+    import numpy as np
+    from oracle import admm, gptq, grid, hessian
+    model, blas, cores = _host_info()
     n_sample = min(X.shape[0], 16384)
     Xs = X[:n_sample]
     t0 = time.perf_counter()
     H, _ = hessian.hessian(Xs, cfg["damp"])
     t_h = time.perf_counter() - t0
+    t0 = time.perf_counter()
     spec = admm.spectral(H)
+    t_eig = time.perf_counter() - t0
     Wf = qz_synth.bf16_bits_to_f32(W_bits[:rows])
     t0 = time.perf_counter()
     admm.admm(H, Wf, cfg["bits"], cfg["group"], iters, cfg["rho0"], cfg["gamma"], cfg["refresh"],
               spec=spec)
     t_loop = time.perf_counter() - t0
     per_iter_layer = t_loop / iters * (cfg["d_o"] / rows)
-    return {"value": 1.0 / per_iter_layer, "unit": "iters/s", "cores": int(cores), "kind": "oracle",
+    t0 = time.perf_counter()
+    R = gptq.inverse_factor_lapack(H)
+    t_r = time.perf_counter() - t0
+    g = min(gptq_rows, rows)
+    s_, z_ = grid.fit_grid_f32(Wf[:g], cfg["bits"], cfg["group"])
+    t0 = time.perf_counter()
+    gptq.gptq(None, Wf[:g], s_, z_, cfg["bits"], cfg["group"], cfg["B"], R=R)
+    t_gl = time.perf_counter() - t0
+    return {"value": 1.0 / per_iter_layer, "unit": "iters/s", "cores": cores, "kind": "oracle",
             "sample": f"{rows} of {cfg['d_o']} rows x {iters} ADMM iterations (fp64 NumPy, H from "
                       f"{n_sample} tokens, eigendecomposition excluded), scaled to the full layer; "
-                      f"loop {t_loop:.2f} s, H build {t_h:.2f} s"}
+                      f"loop {t_loop:.2f} s, H build {t_h:.2f} s",
+            "cpu": model, "blas": blas,
+            "phases_s": {"hessian_16384_tokens": round(t_h, 3), "eigendecomposition": round(t_eig, 3),
+                         "admm_per_iteration_layer": round(per_iter_layer, 3),
+                         "gptq_inverse_factor": round(t_r, 3),
+                         "gptq_loop_layer": round(t_gl * cfg["d_o"] / g, 3),
+                         "gptq_rows_timed": g}}
 
 
 def gptq_work(d_o, d_i, B):
