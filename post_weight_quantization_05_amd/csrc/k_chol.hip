@@ -104,9 +104,12 @@ __global__ __launch_bounds__(NB) void diag_block(double* __restrict__ A, int64_t
     a[j] = lij;
     Ls[i][j] = lij;
     Lc[j][i] = lij;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    // The block is one wavefront, whose LDS operations complete in issue order, so
+    // wavefront-scope ordering makes the column visible to every lane without waiting
+    // for the writes to finish before the reads are issued.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // a[i][l] -= L[i][j] L[l][j] for l > j.  Unguarded: lanes i < j have lij = 0, and the
     // entries l > i it writes lie above the diagonal, which are never read as pivots or
     // column entries (a[j] of lane i < j is replaced by lij = 0) nor stored.
@@ -117,6 +120,9 @@ __global__ __launch_bounds__(NB) void diag_block(double* __restrict__ A, int64_t
 #pragma unroll
   for (int c = 0; c < NB; ++c)
     if (c <= i) A[(k0 + i) * lda + k0 + c] = a[c];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   // Ls holds L (lower; entries above the diagonal are zero); rinv[r] = 1 / L[r][r]
   // X = L^{-1}, lane i holds column i: x[r] = (delta_ri - sum_{q<r} L[r][q] x[q]) / L[r][r]
   double x[NB];
