@@ -62,10 +62,10 @@ __device__ __forceinline__ void tile_coords(int64_t pid, int64_t tm_n, int64_t t
 }
 
 // KB = slab depth: 32 (three workgroups per CU) or 64 (two per CU).  EPI_SUB, whose
-// accumulators are loaded from C up front, runs one workgroup per CU so the registers fit
-// without spilling.
+// accumulators are loaded from C up front, needs more registers: with 32-deep slabs two
+// workgroups per CU fit without spilling (64-deep ones fit only one).
 template <int EPI, bool VEC, int KB>
-__global__ __launch_bounds__(kThreads, EPI == EPI_SUB ? 1 : (KB == 32 ? 3 : 2)) void gemm_nt_kernel(
+__global__ __launch_bounds__(kThreads, EPI == EPI_SUB ? (KB == 32 ? 2 : 1) : (KB == 32 ? 3 : 2)) void gemm_nt_kernel(
     const GemmArgs g) {
   constexpr int BK = KB;
   constexpr int LDK = BK + 4;                       // padded LDS row (floats): rows 4 banks apart
@@ -241,9 +241,9 @@ __global__ __launch_bounds__(kThreads, EPI == EPI_SUB ? 1 : (KB == 32 ? 3 : 2)) 
 // busier, but they pay when the tiles do not fill whole rounds of 768 resident
 // workgroups (the last round runs part-empty) and, as measured, for long K (12288 and
 // 25600 ran slower than with 64-deep slabs); 64-deep slabs with two workgroups per CU
-// are used otherwise.  EPI_SUB (the short-K GPTQ update) uses 64.
+// are used otherwise.  EPI_SUB (the short-K GPTQ update) uses 32 at two workgroups per CU.
 inline int slab_depth(int epi, int64_t tiles, int64_t K) {
-  if (epi == EPI_SUB) return 64;
+  if (epi == EPI_SUB) return 32;
   return (tiles % (3 * 256) == 0 && K <= 8192) ? 32 : 64;
 }
 
