@@ -41,13 +41,13 @@ PEAK_FP64 = 78.6e12        # vector / matrix fp64, FLOP/s
 # SHA-256 of the kernel's source file at the time.  A kernel whose source has changed
 # since reports null.
 TRAFFIC = {
-    "gemm_admm_wupdate1": (5768.5e6, "k_gemm.hip",
-                          "ac76d277882b28e5f7ff5b8d61fceb051405dcf0437d80d5f3c714ec1d118170"),
-    "gemm_admm_wupdate2": (6741.3e6, "k_gemm.hip",
-                          "ac76d277882b28e5f7ff5b8d61fceb051405dcf0437d80d5f3c714ec1d118170"),
+    "gemm_admm_wupdate1": (4993.4e6, "k_gemm.hip",
+                          "4b3b79ff82303147030bf74c271647bb946e67de79935df19ec0b3d93bad1e6a"),
+    "gemm_admm_wupdate2": (6748.4e6, "k_gemm.hip",
+                          "4b3b79ff82303147030bf74c271647bb946e67de79935df19ec0b3d93bad1e6a"),
     "admm_project": (954.3e6, "k_admm.hip",
                     "f23d13c5e3fb9112be82fe528e124b8267a02f258265e5b05ee0dd2e66b14638"),
-    "hessian_gram_bf16": (17351.5e6, "k_hessian.hip",
+    "hessian_gram_bf16": (17579.3e6, "k_hessian.hip",
                          "abe54747eb0646e3cba1d9b30c147fbad51c04e3d4541bd970d7244b514870a0"),
 }
 TRAFFIC_WORKLOAD = "up_4096x12288_w3g128"

@@ -62,8 +62,9 @@ __device__ __forceinline__ void tile_coords(int64_t pid, int64_t tm_n, int64_t t
 }
 
 // KB = slab depth: 32 (three workgroups per CU) or 64 (two per CU).  EPI_SUB, whose
-// accumulators are loaded from C up front, needs more registers: with 32-deep slabs two
-// workgroups per CU fit without spilling (64-deep ones fit only one).
+// accumulators are loaded from C up front, is bounded at two workgroups per CU with 32-deep
+// slabs (64-deep ones fit only one); its interior tiles address C through wave-uniform
+// row pointers, which leaves room for a third.
 template <int EPI, bool VEC, int KB>
 __global__ __launch_bounds__(kThreads, EPI == EPI_SUB ? (KB == 32 ? 2 : 1) : (KB == 32 ? 3 : 2)) void gemm_nt_kernel(
     const GemmArgs g) {
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(kThreads, EPI == EPI_SUB ? (KB == 32 ? 2 : 1) : (KB
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
   const int64_t tm_n = ceil_div(g.M, BM), tn_n = ceil_div(g.N, BN);
@@ -91,12 +92,31 @@ __global__ __launch_bounds__(kThreads, EPI == EPI_SUB ? (KB == 32 ? 2 : 1) : (KB
   const int64_t m0 = tm * BM, n0 = tn * BN;
   const bool interior = VEC && (m0 + BM <= g.M) && (n0 + BN <= g.N) && (g.K % BK == 0);
 
+  // EPI_SUB's interior tiles: C addressed as a wave-uniform row pointer plus one 32-bit lane
+  // offset (4 rows of ldc at most)
+  const bool c_rows = interior && g.ldc <= (int64_t{1} << 28);
   f32x16 acc[2][2];
   if constexpr (EPI == EPI_SUB) {
     // C -= A B is computed as C + (-A) B with C loaded into the accumulators before the
     // K loop (its latency overlaps the first slab; the epilogue is a plain store).
     // Accumulator layout: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column
     // l%32 of the 32 x 32 block.
+    if (c_rows) {
+      // Each register's row pointer is wave-uniform and the lane's offset is the same for
+      // all 64 registers, so the loads (and the stores at the end) need no per-register
+      // addresses: 219 -> 154 registers, and the launch runs at three wavefronts per SIMD.
+      const int lofs = static_cast<int>(4 * (lane >> 5) * g.ldc) + (lane & 31);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float* rowp = g.C + (m0 + wm * 64 + mt * 32 + 8 * (r >> 2) + (r & 3)) * g.ldc +
+                                n0 + wn * 64 + nt * 32;
+            acc[mt][nt][r] = rowp[lofs];
+          }
+    } else {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -108,6 +128,7 @@ __global__ __launch_bounds__(kThreads, EPI == EPI_SUB ? (KB == 32 ? 2 : 1) : (KB
           acc[mt][nt][r] = (row < g.M && col < g.N) ? g.C[row * g.ldc + col] : 0.f;
         }
       }
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -211,6 +232,20 @@ __global__ __launch_bounds__(kThreads, EPI == EPI_SUB ? (KB == 32 ? 2 : 1) : (KB
     __syncthreads();
     if (tid < BM && m0 + tid < g.M)
       g.dpart[(m0 + tid) * tn_n + tn] = red[tid] + red[BM + tid];
+    return;
+  }
+  if (EPI == EPI_SUB && c_rows) {
+    const int lofs = static_cast<int>(4 * (lane >> 5) * g.ldc) + (lane & 31);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float* rowp = g.C + (m0 + wm * 64 + mt * 32 + 8 * (r >> 2) + (r & 3)) * g.ldc + n0 +
+                        wn * 64 + nt * 32;
+          rowp[lofs] = acc[mt][nt][r];
+        }
     return;
   }
 #pragma unroll
