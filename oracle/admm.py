@@ -25,16 +25,20 @@ Readings where the pages are silent (all selectable, defaults first):
 * refresh: per (row, group), min/max of the continuous iterate W = W~ Sigma, forced to
   hold 0, then clamped into the group's initial range [lo_0, hi_0] so a refresh can only
   narrow the grid ("clamped"); "unclamped" takes the fit as is; "from_z" fits W + U Sigma.
+  A range the clamp closes to a point (hi = lo = 0) defines no grid: the group keeps
+  its current scale and zero.
 * refresh at iterations t with t mod k == 0 (k = refresh_every; 0 = never).
 * start: D^0 = RTN(W_hat) on the static fp32 grid of W_hat, U^0 = 0; t runs t0 .. t0+T-1.
 * output: the last discrete iterate and its grid.
 * residuals: r_p = ||W~ - D~^{t+1}||_F and r_d = rho_t ||D~^{t+1} - D~^t||_F (scaled space).
 
-Parity unpinned as a whole trajectory (the pages print no ADMM-Q numbers); the
-pieces are pinned: the W-update against the linear-solve definition, T = 0 and
-rho_0 -> infinity reduce to RTN, on-grid inputs are fixed points, exhaustive
-enumeration bounds the result from below, and the primal residual vanishes under
-the rho schedule.
+Pins: the whole loop against a trajectory derived by hand in exact rational
+arithmetic (tests/golden/admm_trajectory.json: three iterations with the refresh,
+the clamp, the dual rescale and the rho_t indexing all visible); the W-update against
+the linear-solve definition; T = 0 and rho_0 -> infinity reduce to RTN; on-grid inputs
+are fixed points; exhaustive enumeration bounds the result from below; the primal
+residual vanishes under the rho schedule.  The pages print no ADMM-Q numbers, so the
+readings themselves (listed above) are the pages' plainest reading, not pinned values.
 """
 from __future__ import annotations
 
@@ -136,8 +140,17 @@ def admm(H, W_hat_f32, bits, group, iters, rho0, gamma, refresh_every=1, *,
             if refresh in ("clamped", "from_z"):
                 lo = np.maximum(lo, lo0.astype(np.float64))
                 hi = np.minimum(hi, hi0.astype(np.float64))
+            # after the clamp the range can close (hi == lo == 0: a group whose initial
+            # range starts at 0 while the iterate lies entirely on the other side); no
+            # grid has that range, so such a group keeps the grid it had
+            keep = hi <= lo
             zh = None if zero_hints is None else zero_hints[k]
-            scale, zero, n = grid_from_range_f64(lo, hi, bits, zh, tol)
+            # (a stand-in range [-1, 2] for those groups keeps the division finite and its
+            # zero point, (2^b - 1)/3, away from a rounding boundary; it is discarded)
+            s_new, z_new, n = grid_from_range_f64(np.where(keep, -1.0, lo),
+                                                  np.where(keep, 2.0, hi), bits, zh, tol)
+            scale = np.where(keep, scale, s_new).astype(F32)
+            zero = np.where(keep, zero, z_new).astype(np.int64)
             adopted += n
         s_full = np.repeat(scale.astype(np.float64), group, axis=1)
         z_full = np.repeat(zero.astype(np.float64), group, axis=1)
