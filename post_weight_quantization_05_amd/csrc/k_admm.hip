@@ -4,7 +4,8 @@
 // over the weights, one wavefront per (row, group):
 //   grid refresh   -- scale and zero refit from min/max of the continuous iterate
 //                     (W~ Sigma), range forced to hold 0 and, by default, clamped
-//                     into the group's initial range [lo_0, hi_0];
+//                     into the group's initial range [lo_0, hi_0] (a range the clamp
+//                     closes to a point keeps the group's current grid);
 //   D-update       -- C = clamp(rint((W~ + U) Sigma / s) + z): the projection onto the
 //                     grid is round-to-nearest in original coordinates;
 //                     D~ = s (C - z) / Sigma;
@@ -81,8 +82,12 @@ __global__ __launch_bounds__(kThreads) void project_kernel(const AdmmProj p,
         lo = fmaxf(lo, p.lo0[t]);
         hi = fminf(hi, p.hi0[t]);
       }
-      s = (hi - lo) / maxq;
-      z = fminf(fmaxf(__builtin_rintf(-lo / s), 0.f), maxq);
+      // a range the clamp closes to a point (hi = lo = 0) defines no grid: keep the
+      // current one
+      if (hi > lo) {
+        s = (hi - lo) / maxq;
+        z = fminf(fmaxf(__builtin_rintf(-lo / s), 0.f), maxq);
+      }
     }
     const float rs = p.rescale ? p.rho / p.rho_next : 1.0f;
     for (int i = lane; i < p.group; i += 64) {
@@ -247,8 +252,10 @@ __global__ __launch_bounds__(kThreads) void project_reg_kernel(const AdmmProj p,
           lo = fmaxf(lo, p.lo0[t]);
           hi = fminf(hi, p.hi0[t]);
         }
-        s = (hi - lo) / maxq;
-        z = fminf(fmaxf(__builtin_rintf(-lo / s), 0.f), maxq);
+        if (hi > lo) {   // a range closed by the clamp keeps the current grid
+          s = (hi - lo) / maxq;
+          z = fminf(fmaxf(__builtin_rintf(-lo / s), 0.f), maxq);
+        }
       }
       const float rcp = 1.0f / s;
       float un[EPL], mm[EPL];
@@ -409,10 +416,11 @@ int admm_proj_blocks(int64_t G, int64_t d_o) {
 
 int launch_admm_project(const AdmmProj& p, hipStream_t s, const float* inv_sigma) {
   // register-resident path when a group is exactly 64, 128 or 256 columns and every row
-  // start is aligned for the vector loads (U and codes may be the caller's buffers)
+  // start is aligned for the vector loads (U, codes and sigma may be the caller's buffers)
   const bool al = (p.d_i % 4 == 0) && (p.ldw % 4 == 0) && (p.ldm % 4 == 0) &&
                   (reinterpret_cast<uintptr_t>(p.U) % 16 == 0) &&
-                  (reinterpret_cast<uintptr_t>(p.codes) % 4 == 0);
+                  (reinterpret_cast<uintptr_t>(p.codes) % 4 == 0) &&
+                  (reinterpret_cast<uintptr_t>(p.sigma) % 16 == 0);
   const int nb = admm_proj_blocks(p.d_i / p.group, p.d_o);
   if (al && p.group == 128)
     project_reg_kernel<2><<<nb, kThreads, 0, s>>>(p, inv_sigma);

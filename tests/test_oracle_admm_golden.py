@@ -134,7 +134,7 @@ def test_admm_refresh_keeps_grid_when_clamp_closes_range():
     group keeps its grid (scale, zero) and the codes round on it.  With H = I (Sigma = I,
     H~ = I) the W-update is W~ = (W_hat + rho (D - U)) / (1 + rho), checked here in closed
     form."""
-    W = np.array([[0.125, 0.25, 0.375, 0.5]], np.float32)
+    W = np.array([[0.0625, 0.1875, 0.3125, 0.5]], np.float32)
     H = np.eye(4)
     bits, group, rho = 2, 4, 8.0
     lo0, hi0, s0, z0, c0 = admm.initial_grid(W, bits, group)
