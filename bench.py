@@ -154,7 +154,7 @@ def cpu_baseline(cfg, X, W_bits, rows, iters, gptq_rows=1024):
     g = min(gptq_rows, rows)
     s_, z_ = grid.fit_grid_f32(Wf[:g], cfg["bits"], cfg["group"])
     t0 = time.perf_counter()
-    gptq.gptq(None, Wf[:g], s_, z_, cfg["bits"], cfg["group"], cfg["B"], R=R)
+    gptq.gptq(None, Wf[:g], s_, z_, cfg["bits"], cfg["group"], R=R)
     t_gl = time.perf_counter() - t0
     return {"value": 1.0 / per_iter_layer, "unit": "iters/s", "cores": cores, "kind": "oracle",
             "sample": f"{rows} of {cfg['d_o']} rows x {iters} ADMM iterations (fp64 NumPy, H from "
@@ -199,6 +199,7 @@ def run_workload(args, name, steps, warmup, with_cpu, legs=True):
     ws_h = torch.empty(max(q.qz_hessian_workspace(n, d_i), 1), dtype=torch.uint8, device=dev)
     ws_g = torch.empty(q.qz_gptq_workspace(d_o, d_i, B), dtype=torch.uint8, device=dev)
     ws_a = torch.empty(q.qz_admmq_workspace(d_o, d_i, group, iters), dtype=torch.uint8, device=dev)
+    ws_e = torch.empty(q.qz_admmq_prepare_workspace(d_i), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
@@ -214,7 +215,7 @@ def run_workload(args, name, steps, warmup, with_cpu, legs=True):
         e[2].record(stream)
         gp = q.qz_pack(gc, bits)
         e[3].record(stream)
-        V, lam, sig = q.qz_admmq_prepare(hb["H"])
+        V, lam, sig = q.qz_admmq_prepare(hb["H"], ws=ws_e)
         e[4].record(stream)
         out = q.qz_admmq(V, lam, sig, W, bits, group, iters, cfg["rho0"], cfg["gamma"],
                          cfg["refresh"], ws=ws_a, want_U=False)
@@ -297,6 +298,38 @@ def run_workload(args, name, steps, warmup, with_cpu, legs=True):
 
     res_last = recs[-1][1][-1].tolist() if recs else None
     gptq_ms = med["gptq"]
+    # ---- layer-level rooflines: the time each solver would take with every kernel at its
+    # peak (matrix-core products at the fp32 MFMA peak, the fp64 factor at the fp64 peak,
+    # streaming at the HBM peak), against the measured time of the whole call
+    it_roof_s = 4.0 * d_o * d_i * d_i / PEAK_FP32_MFMA + proj_bytes / PEAK_HBM
+    admm_setup_roof_s = 2.0 * d_o * d_i * d_i / PEAK_FP32_MFMA      # P = W~_hat V Lambda
+    admm_roof_ms = (iters * it_roof_s + admm_setup_roof_s) * 1e3
+    gptq_roof_ms = (tr_flops / PEAK_FP32_MFMA + 2.0 / 3.0 * d_i ** 3 / PEAK_FP64) * 1e3
+    hb_roof_ms = hb_flops / PEAK_BF16 * 1e3
+    layer_rl = {
+        "admm_iters_per_s": {"achieved": round(iters_per_s, 3),
+                             "roofline": round(1.0 / it_roof_s, 3),
+                             "frac": round(iters_per_s * it_roof_s, 4),
+                             "roofline_basis": "4 d_o d_i^2 flops at the fp32 MFMA peak + 18 B per "
+                                               "weight at the HBM peak, per iteration"},
+        "admm_weights_per_s": {"achieved": round(d_o * d_i / (admm_call_ms / 1e3), 1),
+                               "roofline": round(d_o * d_i / (admm_roof_ms / 1e3), 1),
+                               "frac": round(admm_roof_ms / admm_call_ms, 4),
+                               "roofline_basis": "set-up product + iterations at their peaks; the "
+                                                 "eigendecomposition (a library call) is excluded "
+                                                 "on both sides"},
+        "gptq_weights_per_s": {"achieved": round(d_o * d_i / (gptq_ms / 1e3), 1),
+                               "roofline": round(d_o * d_i / (gptq_roof_ms / 1e3), 1),
+                               "frac": round(gptq_roof_ms / gptq_ms, 4),
+                               "layer_ms": round(gptq_ms, 3), "roofline_ms": round(gptq_roof_ms, 3),
+                               "roofline_basis": "trailing products at the fp32 MFMA peak + 2/3 d_i^3 "
+                                                 "at the fp64 peak (the in-block loop is not credited)"},
+        "hbuild_tflops": {"achieved": round(hb_flops / (med["hbuild"] / 1e3) / 1e12, 3),
+                          "roofline": round(PEAK_BF16 / 1e12, 3),
+                          "frac": round(hb_roof_ms / med["hbuild"], 4),
+                          "roofline_basis": "n d_i (d_i + 1) flops (upper triangle) at the bf16 "
+                                            "MFMA peak, whole call"},
+    }
     line = {
         "metric": METRIC,
         "value": round(iters_per_s, 3),
@@ -329,6 +362,7 @@ def run_workload(args, name, steps, warmup, with_cpu, legs=True):
             "admm_final_residuals": res_last,
             "kernel_ms": {k: [v[0], round(v[1] / max(v[0], 1), 4)] for k, v in kn.items()},
         },
+        "layer_rooflines": layer_rl,
         "rooflines": rl,
         "roofline": None if dominant is None else {k: dominant[k] for k in
                                                    ("bound", "achieved", "peak", "unit", "frac",
@@ -360,7 +394,7 @@ def run_workload(args, name, steps, warmup, with_cpu, legs=True):
         Xh = X[:16384].view(torch.int16).cpu().numpy().view(np.uint16)
         Wh = W[:args.cpu_rows].view(torch.int16).cpu().numpy().view(np.uint16)
         line["cpu_baseline"] = cpu_baseline(cfg, Xh, Wh, args.cpu_rows, args.cpu_iters)
-    del X, W, H, ws_h, ws_g, ws_a
+    del X, W, H, ws_h, ws_g, ws_a, ws_e
     torch.cuda.empty_cache()
     return line
 

@@ -19,14 +19,15 @@
  * Conventions for every entry point
  * ---------------------------------
  * - All array arguments are DEVICE pointers unless the comment says "host".
- *   The caller owns every buffer; the library never frees caller memory.
- *   Work buffers come from the caller through `ws`/`ws_bytes`, sized by the
- *   matching *_workspace() query and 256-byte aligned (as hipMalloc returns
- *   them); a smaller or misaligned buffer gives QZ_EWORKSPACE.  Other arrays
- *   need only their element type's alignment (vector paths check and fall
- *   back to element access).
- *   (qz_admmq_prepare is the exception: the eigen-solver library it calls
- *   manages its own device memory.)
+ *   The caller owns every buffer; the library never frees caller memory and
+ *   allocates no device memory of its own: work buffers come from the caller
+ *   through `ws`/`ws_bytes`, sized by the matching *_workspace() query and
+ *   256-byte aligned (as hipMalloc returns them); a smaller or misaligned
+ *   buffer gives QZ_EWORKSPACE.  Other arrays need only their element type's
+ *   alignment (vector paths check and fall back to element access).
+ *   Library-owned resources are per host thread and device and created on
+ *   first use: two side streams for the GPTQ factorisation and a rocBLAS
+ *   handle for the eigen-solver (which works in the caller's workspace).
  * - Matrices are dense row-major with the leading dimension equal to the
  *   column count, unless an ld argument is given.
  * - Arguments are checked before anything is enqueued; on a non-OK return the
@@ -52,7 +53,7 @@
 extern "C" {
 #endif
 
-#define QZ_ABI_VERSION 1
+#define QZ_ABI_VERSION 2
 
 typedef enum {
   QZ_OK = 0,
@@ -88,7 +89,8 @@ typedef struct {
  * qz_build_hessian: H = X^T X + lambda I with lambda = damp * mean(diag(X^T X))
  * (ADMM-Q summary, 1. problem formulation; damping: GPTQ tutorial, section 2,
  * "why damping is needed when calibration channels are collinear"), plus
- * diag(H) and Sigma = diag(H)^(-1/2) (ADMM-Q summary, 2., diagonal scaling).
+ * diag(H) and Sigma = diag(H)^(-1/2) (ADMM-Q summary, 2., diagonal scaling),
+ * and optionally the scaled Hessian Sigma H Sigma (unit diagonal).
  *
  *   X       [n x d_i], dtype xt (QZ_BF16: bf16 bit patterns; QZ_F32), n >= 1.
  *   flags   QZ_H_ACCUMULATE: add this call's X^T X to the unfinalised sum
@@ -101,25 +103,34 @@ typedef struct {
  *           symmetric matrix, adds lambda I and writes diag, sigma, lambda.
  *   H       [d_i x d_i] fp32 output (in/out with QZ_H_ACCUMULATE).
  *   diag, sigma  [d_i] fp32 outputs (nullable); lambda_out: 1 fp32 (nullable).
- * Products of bf16 values are exact in fp32; sums are fp32 (matrix cores).
- * Asynchronous.  Non-finite X gives non-finite H, which qz_gptq and
- * qz_admmq_prepare report as QZ_ENONFINITE.                                 */
+ *   H_scaled [d_i x d_i] fp32 output (nullable; not with QZ_H_NO_FINALIZE, must not
+ *             alias H): H_ij sigma_i sigma_j in fp32 with the sigma above.
+ *   ws      qz_hessian_workspace(n, d_i, xt) bytes (split-K partials, staging).
+ * Products of bf16 values are exact in fp32; sums are fp32 (matrix cores); the
+ * split sums are added in a fixed order.  Asynchronous.  Non-finite X gives
+ * non-finite H, which qz_gptq and qz_admmq_prepare report as QZ_ENONFINITE.  */
 #define QZ_H_ACCUMULATE 0x1u
 #define QZ_H_NO_FINALIZE 0x2u
 
 size_t qz_hessian_workspace(int64_t n, int64_t d_i, int32_t xt);
 int qz_build_hessian(const void* X, int32_t xt, int64_t n, int64_t d_i, float damp,
-                     uint32_t flags, float* H, float* diag, float* sigma, float* lambda_out,
-                     void* ws, size_t ws_bytes, hipStream_t stream);
+                     uint32_t flags, float* H, float* diag, float* sigma, float* H_scaled,
+                     float* lambda_out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* -------------------------------------------------------------------- RTN --
  * qz_rtn: round-to-nearest of every weight on its own (ADMM-Q summary, problem
  * statement), on the grid fit from W (or the caller's grid with
  * QZ_GRID_CALLER).  Bit-exact with the fp32 definition above.
  *   W [d_o x d_i] (dtype wt); codes [d_o x d_i] u8 out; scales/zeros
- *   [d_o x d_i/g] out (in with QZ_GRID_CALLER).  SYNC (reports non-finite W). */
+ *   [d_o x d_i/g] out (in with QZ_GRID_CALLER).
+ *   ws: qz_rtn_workspace(d_o, d_i) bytes (the call's status word), 256-byte
+ *   aligned; calls on different streams need different workspaces.
+ *   SYNC (reports non-finite W as QZ_ENONFINITE).                            */
+size_t qz_rtn_workspace(int64_t d_o, int64_t d_i);
 int qz_rtn(const void* W, int32_t wt, int64_t d_o, int64_t d_i, const qz_grid* grid,
-           uint8_t* codes, float* scales, uint8_t* zeros, hipStream_t stream);
+           uint8_t* codes, float* scales, uint8_t* zeros, void* ws, size_t ws_bytes,
+           hipStream_t stream);
+
 
 /* ------------------------------------------------------------------- GPTQ --
  * qz_gptq: GPTQ tutorial, section 3 (Algorithm 1).  R is the upper Cholesky
@@ -143,9 +154,9 @@ int qz_rtn(const void* W, int32_t wt, int64_t d_o, int64_t d_i, const qz_grid* g
  * inverse) and used in fp32; the factorisation runs part of its work on two
  * library-owned side streams (default priority, one pair per host thread and
  * device) that join `stream` before the call goes on, so the call still orders
- * on `stream` only.  SYNC: returns QZ_ENOTPD when a pivot of the factorisation
- * is <= 1e-12 of its diagonal entry (or not finite), and QZ_ENONFINITE for
- * non-finite W_hat.                                                         */
+ * on `stream` only.  SYNC: the codes and the grid are complete when the call
+ * returns; QZ_ENOTPD when a pivot of the factorisation is <= 1e-12 of its
+ * diagonal entry (or not finite), QZ_ENONFINITE for non-finite H or W_hat.   */
 size_t qz_gptq_workspace(int64_t d_o, int64_t d_i, int32_t B);
 int qz_gptq(const float* H, const void* W_hat, int32_t wt, int64_t d_o, int64_t d_i,
             const qz_grid* grid, int32_t B, const int32_t* perm,
@@ -213,9 +224,16 @@ int qz_error_bound(const float* H, int64_t d_i, const int32_t* perm, const float
  * decomposition runs in fp64 in the rocSOLVER library (a library call standing
  * in for host LAPACK); V and Lambda are returned in fp32.
  *   H [d_i x d_i] fp32; V [d_i x d_i] fp32 out, V[j][k] = component j of
- *   eigenvector k; Lambda [d_i] ascending; sigma [d_i].  SYNC.               */
+ *   eigenvector k; Lambda [d_i] ascending; sigma [d_i].
+ *   ws: qz_admmq_prepare_workspace(d_i) bytes, 256-byte aligned: the fp64 copy of
+ *   H~ (8 d_i^2 bytes), the eigenvalue and off-diagonal vectors and the solver
+ *   library's scratch (its size is asked of the library, so the query needs the
+ *   device current; it returns 0 on failure).  d_i <= 46340.
+ *   SYNC: QZ_ENONFINITE for a non-finite H or a non-positive diagonal entry,
+ *   QZ_ESOLVER when the solver fails or does not converge.                    */
+size_t qz_admmq_prepare_workspace(int64_t d_i);
 int qz_admmq_prepare(const float* H, int64_t d_i, float* V, float* Lambda, float* sigma,
-                     hipStream_t stream);
+                     void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* qz_admmq: the ADMM-Q splitting loop in scaled coordinates W~ = W Sigma^{-1}:
  *   for t = t0 .. t0+iters-1, rho_t = rho0 * gamma^t (ADMM-Q summary, 2.,

@@ -10,11 +10,17 @@ grid-refresh item notes that GPTQ keeps the grid fixed).
   by d; the free coordinates move by -d H_F^{-1} e_q / (H_F^{-1})_qq, where H_F^{-1} is
   the inverse curvature of the still-free coordinates, after which q leaves the free
   set (the rank-one downdate of the inverse).
-* gptq -- the blocked route of the same page, section 3 (Algorithm 1): R is the upper
-  Cholesky factor of the damped inverse curvature (R^T R = H^{-1}); within a block of
-  B columns each column is rounded, its scaled error E = (w - q) / R_jj is stored and
-  the rest of the block is corrected by E R[j, j:b]; after the block the remaining
-  columns get one product update W[:, b:] -= E R[a:b, b:].
+* gptq -- the same compensation written with the factor of section 3: R upper with
+  R^T R = H^{-1}.  Row j of R, divided by R_jj, is the compensation direction of
+  section 2 once the columns before j have left the free set (the successive
+  downdates of the inverse are what the Cholesky factorisation of H^{-1} computes,
+  one row at a time), so column k, when its turn comes, holds its original value
+  minus everything the earlier columns sent it:
+      w_k = w_hat_k - sum_{j<k} E_j R_jk,   E_j = (w_j - q_j) / R_jj.
+  This route forms that sum directly for each column (left-looking).  The tutorial's
+  blocks of B columns with one matrix-product update of the later columns per block
+  (section 3) regroup the same terms, so the block size does not enter here; tests
+  check a blocked evaluation against this one.
 
 H passed here already holds the damping (the Hessian builder adds lambda I once).
 """
@@ -83,9 +89,9 @@ def gptq_plain(H, W_hat, scale, zero, bits, group, order=None, clip=True):
     return codes
 
 
-def gptq(H, W_hat, scale, zero, bits, group, B, order=None, clip=True,
-         hint=None, tol=1e-4, R=None, return_E=False):
-    """Blocked route (Algorithm 1 of the GPTQ tutorial page).
+def gptq(H, W_hat, scale, zero, bits, group, order=None, clip=True, hint=None, tol=1e-4, R=None,
+         return_E=False):
+    """The compensation route through R (see the module docstring).
 
     order: processing order of the original columns (None = natural).  The factor R
     belongs to the reordered curvature H[order][:, order]; pass it to skip the
@@ -98,26 +104,19 @@ def gptq(H, W_hat, scale, zero, bits, group, B, order=None, clip=True,
     if R is None:
         Hp = np.asarray(H, np.float64)[np.ix_(order, order)]
         R = inverse_factor(Hp)
-    W = W_hat[:, order].copy()
+    Wp = W_hat[:, order]
     codes = np.zeros((d_o, d_i), np.int64)
-    Eall = np.zeros((d_o, d_i)) if return_E else None
+    E = np.zeros((d_o, d_i), order="F")        # scaled errors, processing order
     adopted = 0
-    for a in range(0, d_i, B):
-        b = min(a + B, d_i)
-        E = np.zeros((d_o, b - a))
-        for j in range(a, b):
-            col = order[j]
-            s, z = _column_grid(scale, zero, group, col)
-            h = None if hint is None else hint[:, col]
-            c, n, _ = round_codes(W[:, j] / s, z, bits, clip, h, tol)
-            adopted += n
-            codes[:, col] = c
-            q = s * (c - z)
-            E[:, j - a] = (W[:, j] - q) / R[j, j]
-            W[:, j:b] -= np.outer(E[:, j - a], R[j, j:b])
-        W[:, b:] -= E @ R[a:b, b:]
-        if return_E:
-            Eall[:, a:b] = E
+    for k in range(d_i):
+        col = order[k]
+        w = Wp[:, k] - E[:, :k] @ R[:k, k]     # every earlier column's compensation
+        s, z = _column_grid(scale, zero, group, col)
+        h = None if hint is None else hint[:, col]
+        c, n, _ = round_codes(w / s, z, bits, clip, h, tol)
+        adopted += n
+        codes[:, col] = c
+        E[:, k] = (w - s * (c - z)) / R[k, k]
     if return_E:
-        return codes, adopted, Eall
+        return codes, adopted, np.ascontiguousarray(E)
     return codes, adopted

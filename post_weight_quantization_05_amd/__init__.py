@@ -81,9 +81,10 @@ def qz_hessian_workspace(n, d_i, xt=_lib.QZ_BF16) -> int:
     return lib().qz_hessian_workspace(n, d_i, xt)
 
 
-def qz_build_hessian(X, damp=0.01, flags=0, H=None, ws=None):
+def qz_build_hessian(X, damp=0.01, flags=0, H=None, ws=None, scaled=False):
     """H = X^T X + lambda I (X [n x d_i] bf16 or fp32 on the GPU).  Returns
-    dict(H, diag, sigma, lam) (tensors; lam is a 1-element tensor)."""
+    dict(H, diag, sigma, lam, H_scaled) (tensors; lam is a 1-element tensor; H_scaled =
+    Sigma H Sigma when scaled=True, else None)."""
     torch = _torch()
     _dev(X, "X")
     n, d = X.shape
@@ -94,15 +95,21 @@ def qz_build_hessian(X, damp=0.01, flags=0, H=None, ws=None):
     diag = torch.empty(d, dtype=torch.float32, device=dev)
     sigma = torch.empty(d, dtype=torch.float32, device=dev)
     lam = torch.empty(1, dtype=torch.float32, device=dev)
+    Hs = torch.empty((d, d), dtype=torch.float32, device=dev) if scaled else None
     need = lib().qz_hessian_workspace(n, d, xt)
     if ws is None:
         ws = _workspace(need, dev)
     _check(lib().qz_build_hessian(_ptr(X), xt, n, d, float(damp), int(flags), _ptr(H), _ptr(diag),
-                                  _ptr(sigma), _ptr(lam), _ptr(ws), ws.numel(), _stream()))
-    return dict(H=H, diag=diag, sigma=sigma, lam=lam)
+                                  _ptr(sigma), _ptr(Hs), _ptr(lam), _ptr(ws), ws.numel(),
+                                  _stream()))
+    return dict(H=H, diag=diag, sigma=sigma, lam=lam, H_scaled=Hs)
 
 
-def qz_rtn(W, bits, group, scales=None, zeros=None):
+def qz_rtn_workspace(d_o, d_i) -> int:
+    return lib().qz_rtn_workspace(d_o, d_i)
+
+
+def qz_rtn(W, bits, group, scales=None, zeros=None, ws=None):
     """Round-to-nearest codes on the grid fit from W (or the given grid)."""
     torch = _torch()
     _dev(W, "W")
@@ -113,9 +120,11 @@ def qz_rtn(W, bits, group, scales=None, zeros=None):
         scales = torch.empty((d_o, G), dtype=torch.float32, device=W.device)
         zeros = torch.empty((d_o, G), dtype=torch.uint8, device=W.device)
     codes = torch.empty((d_o, d_i), dtype=torch.uint8, device=W.device)
+    if ws is None:
+        ws = _workspace(lib().qz_rtn_workspace(d_o, d_i), W.device)
     g = _grid(bits, group, caller)
     _check(lib().qz_rtn(_ptr(W), _dtype_code(W), d_o, d_i, C.byref(g), _ptr(codes), _ptr(scales),
-                        _ptr(zeros), _stream()))
+                        _ptr(zeros), _ptr(ws), ws.numel(), _stream()))
     return codes, scales, zeros
 
 
@@ -203,7 +212,11 @@ def qz_error_bound(H, scales, group, perm=None, rows=False, ws=None):
     return (out.value, rb[:d_o]) if rows else out.value
 
 
-def qz_admmq_prepare(H):
+def qz_admmq_prepare_workspace(d_i) -> int:
+    return lib().qz_admmq_prepare_workspace(d_i)
+
+
+def qz_admmq_prepare(H, ws=None):
     """(V, Lambda, sigma) with Sigma H Sigma = V diag(Lambda) V^T."""
     torch = _torch()
     _dev(H, "H")
@@ -211,7 +224,13 @@ def qz_admmq_prepare(H):
     V = torch.empty((d, d), dtype=torch.float32, device=H.device)
     lam = torch.empty(d, dtype=torch.float32, device=H.device)
     sigma = torch.empty(d, dtype=torch.float32, device=H.device)
-    _check(lib().qz_admmq_prepare(_ptr(H), d, _ptr(V), _ptr(lam), _ptr(sigma), _stream()))
+    if ws is None:
+        need = lib().qz_admmq_prepare_workspace(d)
+        if need == 0:
+            _check(-5)
+        ws = _workspace(need, H.device)
+    _check(lib().qz_admmq_prepare(_ptr(H), d, _ptr(V), _ptr(lam), _ptr(sigma), _ptr(ws), ws.numel(),
+                                  _stream()))
     return V, lam, sigma
 
 

@@ -24,10 +24,11 @@ STATUS_NAMES = {0: "QZ_OK", -1: "QZ_EINVAL", -2: "QZ_ENOTPD", -3: "QZ_ENONFINITE
                 -5: "QZ_ESOLVER", -6: "QZ_EWORKSPACE"}
 
 # every entry point declared in include/qz.h
-EXPORTS = ("qz_hessian_workspace", "qz_build_hessian", "qz_rtn", "qz_gptq_workspace", "qz_gptq",
+EXPORTS = ("qz_hessian_workspace", "qz_build_hessian", "qz_rtn_workspace", "qz_rtn",
+           "qz_gptq_workspace", "qz_gptq",
            "qz_gptq_noclip", "qz_order_workspace", "qz_order", "qz_error_bound_workspace",
            "qz_error_bound",
-           "qz_admmq_prepare", "qz_admmq_workspace", "qz_admmq", "qz_objective_workspace",
+           "qz_admmq_prepare_workspace", "qz_admmq_prepare", "qz_admmq_workspace", "qz_admmq", "qz_objective_workspace",
            "qz_objective", "qz_objective_i32", "qz_local_search_workspace", "qz_local_search",
            "qz_packed_words",
            "qz_pack",
@@ -55,8 +56,9 @@ F = C.c_float
 
 _SIGS = {
     "qz_hessian_workspace": (SZ, [I64, I64, I32]),
-    "qz_build_hessian": (C.c_int, [P, I32, I64, I64, F, U32, P, P, P, P, P, SZ, P]),
-    "qz_rtn": (C.c_int, [P, I32, I64, I64, C.POINTER(QzGrid), P, P, P, P]),
+    "qz_build_hessian": (C.c_int, [P, I32, I64, I64, F, U32, P, P, P, P, P, P, SZ, P]),
+    "qz_rtn_workspace": (SZ, [I64, I64]),
+    "qz_rtn": (C.c_int, [P, I32, I64, I64, C.POINTER(QzGrid), P, P, P, P, SZ, P]),
     "qz_gptq_workspace": (SZ, [I64, I64, I32]),
     "qz_gptq": (C.c_int, [P, P, I32, I64, I64, C.POINTER(QzGrid), I32, P, P, P, P, P, SZ, P]),
     "qz_gptq_noclip": (C.c_int, [P, P, I32, I64, I64, C.POINTER(QzGrid), I32, P, P, P, P, P, SZ,
@@ -65,7 +67,8 @@ _SIGS = {
     "qz_order": (C.c_int, [P, I64, I32, P, P, P, SZ, P]),
     "qz_error_bound_workspace": (SZ, [I64, I64]),
     "qz_error_bound": (C.c_int, [P, I64, P, P, I64, I32, P, P, P, SZ, P]),
-    "qz_admmq_prepare": (C.c_int, [P, I64, P, P, P, P]),
+    "qz_admmq_prepare_workspace": (SZ, [I64]),
+    "qz_admmq_prepare": (C.c_int, [P, I64, P, P, P, P, SZ, P]),
     "qz_admmq_workspace": (SZ, [I64, I64, I32, I32]),
     "qz_admmq": (C.c_int, [P, P, P, P, I32, I64, I64, C.POINTER(QzGrid), C.POINTER(QzAdmm), P, P, P,
                            P, P, P, SZ, P]),

@@ -3,7 +3,6 @@
 // every step runs in the kernels of the k_*.hip translation units.
 #include <cmath>
 #include <cstring>
-#include <mutex>
 #include <string>
 
 #include "qz_internal.h"
@@ -12,22 +11,6 @@ namespace qz {
 
 namespace {
 thread_local std::string g_err;
-
-constexpr int kMaxDevices = 64;
-std::mutex g_flag_mu;
-uint32_t* g_flag[kMaxDevices] = {};
-
-// A 4-byte status word per device for the entry points that take no workspace
-// (qz_rtn); allocated on first use and kept for the life of the process.
-int device_flag(uint32_t** out) {
-  int dev = 0;
-  QZ_HIP(hipGetDevice(&dev));
-  if (dev < 0 || dev >= kMaxDevices) return fail(QZ_EHIP, "device index out of range");
-  std::lock_guard<std::mutex> lk(g_flag_mu);
-  if (!g_flag[dev]) QZ_HIP(hipMalloc(&g_flag[dev], sizeof(uint32_t)));
-  *out = g_flag[dev];
-  return QZ_OK;
-}
 
 int read_flag(const uint32_t* flag, hipStream_t s, uint32_t* host) {
   *host = 0;
@@ -46,6 +29,30 @@ int check_grid(const qz_grid* g, int64_t d_i) {
   if (d_i % g->group_size != 0) return fail(QZ_EINVAL, "grid.group_size must divide d_i");
   if (g->flags & ~QZ_GRID_CALLER) return fail(QZ_EINVAL, "grid.flags has unknown bits");
   return QZ_OK;
+}
+
+// RTN with the status word at `flag` (device memory, one 32-bit word).
+int rtn_run(const void* W, int32_t wt, int64_t d_o, int64_t d_i, const qz_grid* grid,
+            uint8_t* codes, float* scales, uint8_t* zeros, uint32_t* flag, hipStream_t stream) {
+  QZ_TRY(launch_fill_u32(flag, 1, 0u, stream));
+  {
+    ScopedTimer tm(K_GRID_RTN, stream);
+    if (!(grid->flags & QZ_GRID_CALLER)) {
+      QZ_TRY(launch_grid_fit(W, wt, d_o, d_i, grid->group_size, grid->bits, scales, zeros, nullptr,
+                             nullptr, flag, stream));
+    }
+    QZ_TRY(launch_rtn(W, wt, d_o, d_i, grid->group_size, grid->bits, scales, zeros, codes, stream));
+  }
+  uint32_t h = 0;
+  QZ_TRY(read_flag(flag, stream, &h));
+  if (h & FLAG_NONFINITE) return fail(QZ_ENONFINITE, "rtn: non-finite weight");
+  return QZ_OK;
+}
+
+size_t rtn_ws() {
+  Carver c(nullptr);
+  c.take<uint32_t>(1);   // status word
+  return c.used;
 }
 
 size_t objective_ws(int64_t d_o, int64_t d_i) {
@@ -130,11 +137,14 @@ size_t qz_hessian_workspace(int64_t n, int64_t d_i, int32_t xt) {
 }
 
 int qz_build_hessian(const void* X, int32_t xt, int64_t n, int64_t d_i, float damp, uint32_t flags,
-                     float* H, float* diag, float* sigma, float* lambda_out, void* ws,
-                     size_t ws_bytes, hipStream_t stream) {
+                     float* H, float* diag, float* sigma, float* H_scaled, float* lambda_out,
+                     void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!valid_dtype(xt)) return fail(QZ_EINVAL, "build_hessian: bad dtype");
   if (n < 0 || d_i < 1) return fail(QZ_EINVAL, "build_hessian: need n >= 0 and d_i >= 1");
   if (!H || (n > 0 && !X)) return fail(QZ_EINVAL, "build_hessian: null pointer");
+  if (H_scaled && H_scaled == H) return fail(QZ_EINVAL, "build_hessian: H_scaled must not alias H");
+  if (H_scaled && (flags & QZ_H_NO_FINALIZE))
+    return fail(QZ_EINVAL, "build_hessian: H_scaled needs a finalised H (no QZ_H_NO_FINALIZE)");
   if (!(damp >= 0.f) || !std::isfinite(damp)) return fail(QZ_EINVAL, "build_hessian: damp must be finite and >= 0");
   if (flags & ~(QZ_H_ACCUMULATE | QZ_H_NO_FINALIZE)) return fail(QZ_EINVAL, "build_hessian: unknown flags");
   const size_t need = hessian_ws_bytes(n, d_i, xt);
@@ -142,32 +152,29 @@ int qz_build_hessian(const void* X, int32_t xt, int64_t n, int64_t d_i, float da
   if (reinterpret_cast<uintptr_t>(ws) % 256 != 0)
     return fail(QZ_EWORKSPACE, "build_hessian: workspace must be 256-byte aligned");
   set_error("");
-  return hessian_build(X, xt, n, d_i, damp, flags, H, diag, sigma, lambda_out, ws, ws_bytes, stream);
+  return hessian_build(X, xt, n, d_i, damp, flags, H, diag, sigma, H_scaled, lambda_out, ws,
+                       ws_bytes, stream);
 }
 
 // ------------------------------------------------------------------ RTN
+size_t qz_rtn_workspace(int64_t d_o, int64_t d_i) {
+  if (d_o < 0 || d_i < 1) return 0;
+  return rtn_ws();
+}
+
 int qz_rtn(const void* W, int32_t wt, int64_t d_o, int64_t d_i, const qz_grid* grid,
-           uint8_t* codes, float* scales, uint8_t* zeros, hipStream_t stream) {
+           uint8_t* codes, float* scales, uint8_t* zeros, void* ws, size_t ws_bytes,
+           hipStream_t stream) {
   if (!valid_dtype(wt)) return fail(QZ_EINVAL, "rtn: bad dtype");
   if (d_o < 0 || d_i < 1) return fail(QZ_EINVAL, "rtn: need d_o >= 0 and d_i >= 1");
   QZ_TRY(check_grid(grid, d_i));
+  if (ws_bytes < rtn_ws() || !ws) return fail(QZ_EWORKSPACE, "rtn: workspace too small");
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0)
+    return fail(QZ_EWORKSPACE, "rtn: workspace must be 256-byte aligned");
   if (d_o == 0) return QZ_OK;
   if (!W || !codes || !scales || !zeros) return fail(QZ_EINVAL, "rtn: null pointer");
-  uint32_t* flag = nullptr;
-  QZ_TRY(device_flag(&flag));
-  QZ_TRY(launch_fill_u32(flag, 1, 0u, stream));
-  {
-    ScopedTimer tm(K_GRID_RTN, stream);
-    if (!(grid->flags & QZ_GRID_CALLER)) {
-      QZ_TRY(launch_grid_fit(W, wt, d_o, d_i, grid->group_size, grid->bits, scales, zeros, nullptr,
-                             nullptr, flag, stream));
-    }
-    QZ_TRY(launch_rtn(W, wt, d_o, d_i, grid->group_size, grid->bits, scales, zeros, codes, stream));
-  }
-  uint32_t h = 0;
-  QZ_TRY(read_flag(flag, stream, &h));
-  if (h & FLAG_NONFINITE) return fail(QZ_ENONFINITE, "rtn: non-finite weight");
-  return QZ_OK;
+  set_error("");
+  return rtn_run(W, wt, d_o, d_i, grid, codes, scales, zeros, static_cast<uint32_t*>(ws), stream);
 }
 
 // ------------------------------------------------------------------ GPTQ
@@ -265,6 +272,8 @@ static int gptq_run(const float* H, const void* W_hat, int32_t wt, int64_t d_o, 
     }
     if (Aend < d_i) QZ_TRY(update(E, Aend - A, Aend, d_i - Aend, A));   // every later column
   }
+  // SYNC: the codes and the grid are complete when the call returns
+  QZ_HIP(hipStreamSynchronize(stream));
   return QZ_OK;
 }
 
@@ -381,13 +390,23 @@ int qz_error_bound(const float* H, int64_t d_i, const int32_t* perm, const float
 }
 
 // ------------------------------------------------------------------ ADMM-Q
-int qz_admmq_prepare(const float* H, int64_t d_i, float* V, float* Lambda, float* sigma,
-                     hipStream_t stream) {
+size_t qz_admmq_prepare_workspace(int64_t d_i) {
+  if (d_i < 1) return 0;
+  size_t b = 0;
+  if (eig_ws_bytes(d_i, &b) != QZ_OK) return 0;
+  return b;
+}
+
+int qz_admmq_prepare(const float* H, int64_t d_i, float* V, float* Lambda, float* sigma, void* ws,
+                     size_t ws_bytes, hipStream_t stream) {
   if (d_i < 1) return fail(QZ_EINVAL, "admmq_prepare: d_i must be >= 1");
   if (!H || !V || !Lambda || !sigma) return fail(QZ_EINVAL, "admmq_prepare: null pointer");
+  if (!ws) return fail(QZ_EWORKSPACE, "admmq_prepare: workspace too small");
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0)
+    return fail(QZ_EWORKSPACE, "admmq_prepare: workspace must be 256-byte aligned");
   set_error("");
   ScopedTimer tm(K_EIG, stream);
-  return eig_scaled(H, d_i, V, Lambda, sigma, stream);
+  return eig_scaled(H, d_i, V, Lambda, sigma, ws, ws_bytes, stream);
 }
 
 size_t qz_admmq_workspace(int64_t d_o, int64_t d_i, int32_t group_size, int32_t iters) {

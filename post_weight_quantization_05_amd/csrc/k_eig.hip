@@ -3,9 +3,15 @@
 // here of H~ = Sigma H Sigma with Sigma = diag(H)^(-1/2)).  A one-time set-up step:
 // H~ is formed in fp64 on the device and handed to rocSOLVER's divide-and-conquer
 // symmetric eigensolver (a library call standing in for host LAPACK); V and Lambda
-// come back in fp32.
+// come back in fp32.  Every device byte the call uses -- the fp64 matrix, the
+// eigenvalue and off-diagonal vectors, the solver's own scratch -- comes from the
+// caller's workspace: the solver's scratch size is asked of the library once per
+// size (its device-memory size query) and handed to it with rocblas_set_workspace.
+// The rocBLAS handle is created once per host thread and device and kept.
 #include <rocblas/rocblas.h>
 #include <rocsolver/rocsolver.h>
+
+#include <vector>
 
 #include "qz_internal.h"
 
@@ -71,87 +77,137 @@ inline unsigned grid_for(int64_t n) {
   return static_cast<unsigned>(b);
 }
 
+struct SolverHandle {
+  int device = -1;
+  rocblas_handle h = nullptr;
+};
+
+// One rocBLAS handle per host thread and device, created on first use and kept (like the
+// R factor's side streams): creating a handle per call would cost more than a small solve.
+int solver_handle(rocblas_handle* out) {
+  int dev = 0;
+  QZ_HIP(hipGetDevice(&dev));
+  thread_local std::vector<SolverHandle> cache;
+  for (const SolverHandle& c : cache)
+    if (c.device == dev) {
+      *out = c.h;
+      return QZ_OK;
+    }
+  SolverHandle c;
+  c.device = dev;
+  if (rocblas_create_handle(&c.h) != rocblas_status_success)
+    return fail(QZ_ESOLVER, "admmq_prepare: rocblas_create_handle failed");
+  cache.push_back(c);
+  *out = c.h;
+  return QZ_OK;
+}
+
+// Scratch bytes rocsolver_dsyevd needs for an n x n problem (the library's size-query
+// mode: nothing runs and no pointer is dereferenced, but the argument checks want
+// non-null pointers, so host dummies stand in).
+int solver_scratch(rocblas_handle h, int64_t n, size_t* bytes) {
+  static double dummy[4];
+  static rocblas_int dummy_info;
+  if (rocblas_start_device_memory_size_query(h) != rocblas_status_success)
+    return fail(QZ_ESOLVER, "admmq_prepare: solver size query failed to start");
+  const rocblas_status st = rocsolver_dsyevd(h, rocblas_evect_original, rocblas_fill_upper,
+                                             static_cast<rocblas_int>(n), dummy,
+                                             static_cast<rocblas_int>(n), dummy, dummy,
+                                             &dummy_info);
+  size_t sz = 0;
+  const rocblas_status st2 = rocblas_stop_device_memory_size_query(h, &sz);
+  if ((st != rocblas_status_success && st != rocblas_status_size_increased &&
+       st != rocblas_status_size_unchanged) ||
+      st2 != rocblas_status_success)
+    return fail(QZ_ESOLVER, "admmq_prepare: solver size query failed (" + std::to_string(int(st)) +
+                                ", " + std::to_string(int(st2)) + ")");
+  *bytes = sz;
+  return QZ_OK;
+}
+
+struct EigLayout {
+  size_t A, D, E, sig64, info, flag, scratch, total;
+};
+
+EigLayout eig_layout(int64_t d, size_t scratch) {
+  EigLayout l;
+  Carver c(nullptr);
+  l.A = c.used;     c.take<double>(static_cast<size_t>(d) * d);
+  l.D = c.used;     c.take<double>(static_cast<size_t>(d));
+  l.E = c.used;     c.take<double>(static_cast<size_t>(d));
+  l.sig64 = c.used; c.take<double>(static_cast<size_t>(d));
+  l.info = c.used;  c.take<rocblas_int>(1);
+  l.flag = c.used;  c.take<uint32_t>(1);
+  l.scratch = c.used;
+  l.total = align256(c.used + scratch);
+  return l;
+}
+
 }  // namespace
 
-int eig_scaled(const float* H, int64_t d, float* V, float* Lambda, float* sigma, hipStream_t s) {
+int eig_ws_bytes(int64_t d, size_t* bytes) {
   if (d > 46340) return fail(QZ_EINVAL, "admmq_prepare: d_i too large for the eigensolver");
-  double* A = nullptr;
-  double* D = nullptr;
-  double* E = nullptr;
-  double* sig64 = nullptr;
-  int* info = nullptr;
-  uint32_t* flag = nullptr;
+  rocblas_handle h = nullptr;
+  QZ_TRY(solver_handle(&h));
+  size_t scratch = 0;
+  QZ_TRY(solver_scratch(h, d, &scratch));
+  *bytes = eig_layout(d, scratch).total;
+  return QZ_OK;
+}
+
+int eig_scaled(const float* H, int64_t d, float* V, float* Lambda, float* sigma, void* ws,
+               size_t ws_bytes, hipStream_t s) {
+  if (d > 46340) return fail(QZ_EINVAL, "admmq_prepare: d_i too large for the eigensolver");
   rocblas_handle handle = nullptr;
-  int rc = QZ_OK;
-  auto cleanup = [&]() {
-    if (handle) rocblas_destroy_handle(handle);
-    (void)hipFree(A);
-    (void)hipFree(D);
-    (void)hipFree(E);
-    (void)hipFree(sig64);
-    (void)hipFree(info);
-    (void)hipFree(flag);
-  };
-  do {
-    hipError_t e = hipMalloc(reinterpret_cast<void**>(&A), sizeof(double) * d * d);
-    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&D), sizeof(double) * d);
-    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&E), sizeof(double) * d);
-    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&sig64), sizeof(double) * d);
-    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&info), sizeof(int));
-    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&flag), sizeof(uint32_t));
-    if (e != hipSuccess) {
-      rc = fail(QZ_EHIP, std::string("admmq_prepare: device allocation failed: ") +
-                             hipGetErrorName(e) + " " + hipGetErrorString(e));
-      break;
-    }
-    if ((rc = launch_fill_u32(flag, 1, 0u, s)) != QZ_OK) break;
-    sigma_kernel<<<grid_for(d), kThreads, 0, s>>>(H, d, sigma, sig64, flag);
-    if ((rc = check_launch("eig.sigma")) != QZ_OK) break;
-    scale_kernel<<<grid_for(d * d), kThreads, 0, s>>>(H, d, sig64, A, flag);
-    if ((rc = check_launch("eig.scale")) != QZ_OK) break;
-    uint32_t hflag = 0;
-    if (hipMemcpyAsync(&hflag, flag, sizeof(uint32_t), hipMemcpyDeviceToHost, s) != hipSuccess ||
-        hipStreamSynchronize(s) != hipSuccess) {
-      rc = fail(QZ_EHIP, "admmq_prepare: sync failed");
-      break;
-    }
-    if (hflag & FLAG_NONFINITE) {
-      rc = fail(QZ_ENONFINITE, "admmq_prepare: H has a non-finite entry or a non-positive diagonal");
-      break;
-    }
-    if (rocblas_create_handle(&handle) != rocblas_status_success ||
-        rocblas_set_stream(handle, s) != rocblas_status_success) {
-      rc = fail(QZ_ESOLVER, "admmq_prepare: rocblas handle");
-      break;
-    }
-    rocblas_status st = rocsolver_dsyevd(handle, rocblas_evect_original, rocblas_fill_upper,
-                                         static_cast<rocblas_int>(d), A, static_cast<rocblas_int>(d),
-                                         D, E, info);
-    if (st != rocblas_status_success) {
-      rc = fail(QZ_ESOLVER, "admmq_prepare: rocsolver_dsyevd status " + std::to_string(int(st)));
-      break;
-    }
-    int hinfo = 0;
-    if (hipMemcpyAsync(&hinfo, info, sizeof(int), hipMemcpyDeviceToHost, s) != hipSuccess ||
-        hipStreamSynchronize(s) != hipSuccess) {
-      rc = fail(QZ_EHIP, "admmq_prepare: sync failed");
-      break;
-    }
-    if (hinfo != 0) {
-      rc = fail(QZ_ESOLVER, "admmq_prepare: eigensolver did not converge (info " +
+  QZ_TRY(solver_handle(&handle));
+  size_t scratch = 0;
+  QZ_TRY(solver_scratch(handle, d, &scratch));
+  const EigLayout l = eig_layout(d, scratch);
+  if (!ws || ws_bytes < l.total) return fail(QZ_EWORKSPACE, "admmq_prepare: workspace too small");
+  char* base = static_cast<char*>(ws);
+  double* A = reinterpret_cast<double*>(base + l.A);
+  double* D = reinterpret_cast<double*>(base + l.D);
+  double* E = reinterpret_cast<double*>(base + l.E);
+  double* sig64 = reinterpret_cast<double*>(base + l.sig64);
+  rocblas_int* info = reinterpret_cast<rocblas_int*>(base + l.info);
+  uint32_t* flag = reinterpret_cast<uint32_t*>(base + l.flag);
+
+  QZ_TRY(launch_fill_u32(flag, 1, 0u, s));
+  sigma_kernel<<<grid_for(d), kThreads, 0, s>>>(H, d, sigma, sig64, flag);
+  QZ_TRY(check_launch("eig.sigma"));
+  scale_kernel<<<grid_for(d * d), kThreads, 0, s>>>(H, d, sig64, A, flag);
+  QZ_TRY(check_launch("eig.scale"));
+  uint32_t hflag = 0;
+  QZ_HIP(hipMemcpyAsync(&hflag, flag, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
+  QZ_HIP(hipStreamSynchronize(s));
+  if (hflag & FLAG_NONFINITE)
+    return fail(QZ_ENONFINITE, "admmq_prepare: H has a non-finite entry or a non-positive diagonal");
+
+  // the solver runs on the caller's stream, in the caller's memory; the handle is
+  // detached from that memory again before the call returns
+  if (rocblas_set_stream(handle, s) != rocblas_status_success ||
+      rocblas_set_workspace(handle, scratch ? base + l.scratch : nullptr, scratch) !=
+          rocblas_status_success)
+    return fail(QZ_ESOLVER, "admmq_prepare: could not attach the solver workspace");
+  const rocblas_status st = rocsolver_dsyevd(handle, rocblas_evect_original, rocblas_fill_upper,
+                                             static_cast<rocblas_int>(d), A,
+                                             static_cast<rocblas_int>(d), D, E, info);
+  int hinfo = 0;
+  const hipError_t ec = hipMemcpyAsync(&hinfo, info, sizeof(int), hipMemcpyDeviceToHost, s);
+  const hipError_t es = hipStreamSynchronize(s);
+  rocblas_set_workspace(handle, nullptr, 0);
+  if (st != rocblas_status_success)
+    return fail(QZ_ESOLVER, "admmq_prepare: rocsolver_dsyevd status " + std::to_string(int(st)));
+  if (ec != hipSuccess || es != hipSuccess) return fail(QZ_EHIP, "admmq_prepare: sync failed");
+  if (hinfo != 0)
+    return fail(QZ_ESOLVER, "admmq_prepare: eigensolver did not converge (info " +
                                 std::to_string(hinfo) + ")");
-      break;
-    }
-    dim3 grid(static_cast<unsigned>(ceil_div(d, 32)), static_cast<unsigned>(ceil_div(d, 32)));
-    export_kernel<<<grid, kThreads, 0, s>>>(A, D, d, V, Lambda);
-    if ((rc = check_launch("eig.export")) != QZ_OK) break;
-    if (hipStreamSynchronize(s) != hipSuccess) {
-      rc = fail(QZ_EHIP, "admmq_prepare: sync failed");
-      break;
-    }
-  } while (false);
-  cleanup();
-  return rc;
+  dim3 grid(static_cast<unsigned>(ceil_div(d, 32)), static_cast<unsigned>(ceil_div(d, 32)));
+  export_kernel<<<grid, kThreads, 0, s>>>(A, D, d, V, Lambda);
+  QZ_TRY(check_launch("eig.export"));
+  // the workspace holds the fp64 factors until the export has read them
+  QZ_HIP(hipStreamSynchronize(s));
+  return QZ_OK;
 }
 
 }  // namespace qz

@@ -1,21 +1,23 @@
-// GPTQ in-block column loop (GPTQ tutorial, section 3, Algorithm 1, the inner loop):
-// for every column j of the block [a, b) in the common order,
-//     q_j      = grid value of round-to-nearest(w_j)        (the row's static grid)
-//     E[:, j]  = (w_j - q_j) / R_jj
-//     w[j:b]  -= E[:, j] R[j, j:b]
-// The rows are independent (they share only R), so a workgroup owns 64 rows and runs
-// the loop for all of them in lock-step.  Four lanes of a quad share one row; lane q
-// of the quad keeps columns q, q+4, q+8, ... of the block in registers, so the row's
-// 128-column block never leaves the register file.  At step j the owner lane of the
-// column rounds it (IEEE fp32 division, half-to-even), forms E, and a DPP quad
-// broadcast hands E to the other three lanes; each lane then updates its remaining
-// columns with R[j, :] read from LDS (stored lane-deinterleaved and padded, so the
-// four distinct slices a wavefront reads per instruction, and the staging writes, are
-// free of bank conflicts).  The workgroup's set-up stages R's block and each row's
-// (scale, zero) per column with many global loads in flight (clamped addresses, selected
-// afterwards); at the end E leaves through LDS as whole rows and, in natural order, the
-// codes as 16-byte row pieces.  The trailing update of the columns after the block is
-// the separate matrix-core GEMM (k_gemm.hip).
+// GPTQ in-block column kernel (GPTQ tutorial, section 3: the column-by-column part of
+// the blocked quantizer; section 2 gives the compensation it applies).  Inside a block
+// of at most 128 columns the columns are fixed one after another in the common order:
+// every row rounds its current value of the column on its static grid, and the error
+// divided by the pivot R_jj (kept per row as the block's E) is passed on to the block's
+// remaining columns along row j of R.  Columns after the block receive all of the
+// block's errors at once, through the separate matrix-core product in k_gemm.hip.
+//
+// The rows are independent (they share only R), so a workgroup owns 64 rows and steps
+// through the columns for all of them together.  Four lanes of a quad share one row;
+// lane q of the quad keeps columns q, q+4, q+8, ... of the block in registers, so the
+// row's block never leaves the register file.  At step j the lane holding column j
+// rounds it (IEEE fp32 division, half-to-even) and forms the scaled error, a DPP quad
+// broadcast hands it to the other three lanes, and each lane updates its columns with
+// R's row j read from LDS (stored lane-deinterleaved and padded, so the four distinct
+// slices a wavefront reads per instruction, and the staging writes, are free of bank
+// conflicts).  The workgroup's set-up stages R's block and each row's (scale, zero) per
+// column with many global loads in flight (clamped addresses, selected afterwards); at
+// the end E leaves through LDS as whole rows and, in natural order, the codes as
+// 16-byte row pieces.
 #include "qz_internal.h"
 
 namespace qz {

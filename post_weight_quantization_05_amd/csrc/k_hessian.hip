@@ -4,19 +4,23 @@
 // summary, 2. key components).
 //
 // X is [n x d] bf16, row-major (tokens are rows), so the contraction index runs
-// along the OUTER dimension of both operands.  Each workgroup owns one 128 x 128
-// tile of the upper triangle (I <= J; the lower triangle is mirrored afterwards, so
-// only n d (d + 1) flops are spent up to tile granularity) and one contiguous token
-// range (split-K when the triangle alone cannot fill the chip).  A K-step stages 64
-// tokens: every thread loads an 8-token x 8-channel bf16 block with 16-byte loads,
-// transposes it in registers (perm-style half-word shuffles) and stores it to LDS as
-// channel-major rows of 64 tokens, so that each lane then reads the 8 consecutive
-// tokens that v_mfma_f32_32x32x16_bf16 wants per operand with one 16-byte LDS read.
-// bf16 x bf16 products are exact in fp32; sums accumulate in fp32 in the MFMA.
+// along the OUTER dimension of both operands.  Each workgroup of the main kernel owns
+// one 256 x 256 tile of the upper triangle (I <= J; only n d (d + 1) flops are spent up
+// to tile granularity) and one contiguous token range (split-K when the triangle alone
+// cannot fill the chip).  X streams from HBM into LDS with global_load_lds (no register
+// round trip), token-major with a chunk swizzle, and ds_read_b64_tr_b16 hands every lane
+// the 8 consecutive tokens of one channel that v_mfma_f32_32x32x16_bf16 wants per
+// operand (the transpose happens in the LDS read).  bf16 x bf16 products are exact in
+// fp32; sums accumulate in fp32 in the MFMA.  X whose rows are not 16-byte aligned goes
+// through a kernel that stages the same token-major tiles with register loads (element
+// loads at the ragged edge) instead of the direct copies.
 //
-// Partial tiles of the splits go to the workspace and are summed in a fixed order
-// (deterministic), then the finalize kernels add lambda to the diagonal, write
-// diag/sigma/lambda and mirror the upper triangle.
+// Epilogue: the split partials are summed in a fixed order (deterministic) in one pass
+// that also mirrors each sub-block into the lower triangle through LDS and copies the
+// raw diagonal out contiguously; one small kernel then forms lambda from that diagonal
+// (the global mean needs every diagonal tile, hence the second launch) and writes
+// H_ii + lambda, diag and sigma; H_scaled = Sigma H Sigma is a third pass, only when
+// asked for.
 #include "qz_internal.h"
 
 namespace qz {
@@ -354,51 +358,93 @@ __global__ void schedule_kernel(int64_t T, int32_t* __restrict__ tiles) {
 
 constexpr int kSmall = 256;   // threads of the auxiliary kernels below
 
-// Sum the split partials of every upper tile into H (adding the previous raw sum when
-// accumulating), fixed order.  One thread per tile element.
-__global__ __launch_bounds__(kSmall) void gram_reduce_kernel(const float* __restrict__ partial,
-                                                             int64_t S, int64_t n_tiles,
-                                                             const int32_t* __restrict__ tiles,
-                                                             int64_t d, int accumulate,
-                                                             float* __restrict__ H) {
+// Split-K reduction and mirror in one pass.  One workgroup per 64 x 64 sub-block of an
+// upper tile: the S partials of each element are summed in split order (deterministic;
+// the previous raw sum is added when accumulating) and written to the upper triangle;
+// the sub-block then goes through LDS and is written transposed into the lower triangle
+// (both writes coalesced), and diagonal elements are also copied to `dg` (contiguous,
+// for the damping kernel).  Sub-blocks below the diagonal of a diagonal tile hold
+// nothing the upper triangle does not, and return at once.
+constexpr int RSB = 64;   // sub-block edge
+__global__ __launch_bounds__(kSmall) void reduce_mirror_kernel(const float* __restrict__ partial,
+                                                               int64_t S, int64_t n_tiles,
+                                                               const int32_t* __restrict__ tiles,
+                                                               int64_t d, int accumulate,
+                                                               int mirror, float* __restrict__ H,
+                                                               float* __restrict__ dg) {
+  __shared__ float tr[RSB][RSB + 1];
+  constexpr int per = HT / RSB;
+  const int64_t t = blockIdx.x / (per * per);
+  const int sb = static_cast<int>(blockIdx.x % (per * per));
+  const int sbi = sb / per, sbj = sb % per;
+  const int64_t I = tiles[2 * t], J = tiles[2 * t + 1];
+  if (I == J && sbi > sbj) return;
+  const int64_t r0 = I * HT + sbi * RSB, c0 = J * HT + sbj * RSB;
+  if (r0 >= d || c0 >= d) return;
+  const int tx = threadIdx.x % RSB, ty = threadIdx.x / RSB;
+  constexpr int rstep = kSmall / RSB;
   const int64_t per_tile = static_cast<int64_t>(HT) * HT;
-  const int64_t total = n_tiles * per_tile;
-  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t t = e / per_tile, rc = e % per_tile;
-    const int64_t i = static_cast<int64_t>(tiles[2 * t]) * HT + rc / HT;
-    const int64_t j = static_cast<int64_t>(tiles[2 * t + 1]) * HT + rc % HT;
-    if (i >= d || j >= d) continue;
-    float s = 0.f;
-    for (int64_t sp = 0; sp < S; ++sp) s += partial[(sp * n_tiles + t) * per_tile + rc];
-    if (accumulate) s += H[i * d + j];
-    H[i * d + j] = s;
+  for (int rr = ty; rr < RSB; rr += rstep) {
+    const int64_t i = r0 + rr, j = c0 + tx;
+    const int64_t off = static_cast<int64_t>(sbi * RSB + rr) * HT + sbj * RSB + tx;
+    float v = 0.f;
+    for (int64_t sp = 0; sp < S; ++sp) v += partial[(sp * n_tiles + t) * per_tile + off];
+    if (i < d && j < d && i <= j) {
+      if (accumulate) v += H[i * d + j];
+      H[i * d + j] = v;
+      if (i == j) dg[i] = v;
+    }
+    tr[rr][tx] = v;
+  }
+  if (!mirror) return;
+  __syncthreads();
+  for (int rr = ty; rr < RSB; rr += rstep) {
+    const int64_t i = c0 + rr, j = r0 + tx;   // destination (i, j) below the diagonal
+    if (i < d && j < d && i > j) H[i * d + j] = tr[tx][rr];
   }
 }
 
-// lambda = damp * mean(diag); H_ii += lambda; diag, sigma.  One workgroup, fp64
-// sums in a fixed order.
-__global__ __launch_bounds__(kSmall) void lambda_kernel(float* __restrict__ H, int64_t d,
-                                                        float damp, float* __restrict__ diag,
-                                                        float* __restrict__ sigma,
-                                                        float* __restrict__ lambda_out) {
-  __shared__ double red[kSmall];
+// lambda = damp * mean(diag), summed in fp64 in a fixed order by one workgroup over the
+// raw diagonal (contiguous `dg`, or the diagonal of H when dg is null); then
+// H_ii = raw_ii + lambda, diag, sigma = 1 / sqrt(H_ii), lambda_out.
+constexpr int kLam = 1024;
+__global__ __launch_bounds__(kLam) void lambda_kernel(float* __restrict__ H, int64_t d,
+                                                      const float* __restrict__ dg, float damp,
+                                                      float* __restrict__ diag,
+                                                      float* __restrict__ sigma,
+                                                      float* __restrict__ lambda_out,
+                                                      float* __restrict__ sig_ws) {
+  __shared__ double red[kLam];
   double s = 0.0;
-  for (int64_t i = threadIdx.x; i < d; i += blockDim.x) s += static_cast<double>(H[i * d + i]);
+  for (int64_t i = threadIdx.x; i < d; i += kLam)
+    s += static_cast<double>(dg ? dg[i] : H[i * d + i]);
   red[threadIdx.x] = s;
   __syncthreads();
-  for (int w = kSmall / 2; w > 0; w >>= 1) {
+  for (int w = kLam / 2; w > 0; w >>= 1) {
     if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
     __syncthreads();
   }
   const float lam = static_cast<float>(static_cast<double>(damp) * (red[0] / static_cast<double>(d)));
-  for (int64_t i = threadIdx.x; i < d; i += blockDim.x) {
-    const float h = H[i * d + i] + lam;
+  for (int64_t i = threadIdx.x; i < d; i += kLam) {
+    const float h = (dg ? dg[i] : H[i * d + i]) + lam;
+    const float sg = 1.0f / sqrtf(h);
     H[i * d + i] = h;
     if (diag) diag[i] = h;
-    if (sigma) sigma[i] = 1.0f / sqrtf(h);
+    if (sigma) sigma[i] = sg;
+    sig_ws[i] = sg;
   }
   if (threadIdx.x == 0 && lambda_out) *lambda_out = lam;
+}
+
+// H_scaled = Sigma H Sigma in fp32 from the sigma the damping kernel wrote (Sigma_i =
+// 1 / sqrt(H_ii), the rounding of the sigma output), one workgroup per row.
+__global__ __launch_bounds__(kSmall) void scaled_kernel(const float* __restrict__ H, int64_t d,
+                                                        const float* __restrict__ sg,
+                                                        float* __restrict__ Hs) {
+  for (int64_t i = blockIdx.x; i < d; i += gridDim.x) {
+    const float si = sg[i];
+    for (int64_t j = threadIdx.x; j < d; j += kSmall) Hs[i * d + j] = H[i * d + j] * si * sg[j];
+  }
 }
 
 // H[j][i] = H[i][j] for i < j, through 32 x 32 LDS tiles (coalesced both ways).
@@ -482,19 +528,27 @@ int launch_transpose_f32(const float* in, int64_t rows, int64_t cols, int64_t ld
   return check_launch("transpose_f32");
 }
 
+// Workspace: [X^T staging (fp32 input) | schedule, split partials, raw diagonal (bf16)]
+// followed by sigma (d floats) for the H_scaled pass.
 size_t hessian_ws_bytes(int64_t n, int64_t d, int xt) {
-  if (xt == QZ_F32) return align256(static_cast<size_t>(round_up(d, 4)) * round_up(n, 4) * 4);
+  const size_t vec = align256(static_cast<size_t>(d) * sizeof(float));
+  if (xt == QZ_F32) return align256(static_cast<size_t>(round_up(d, 4)) * round_up(n, 4) * 4) + vec;
   const HPlan p = plan_for(n, d);
-  return p.tiles_bytes + p.partial_bytes;
+  return p.tiles_bytes + p.partial_bytes + 2 * vec;
 }
 
 int hessian_build(const void* X, int xt, int64_t n, int64_t d, float damp, uint32_t flags,
-                  float* H, float* diag, float* sigma, float* lambda_out, void* ws,
-                  size_t ws_bytes, hipStream_t s) {
+                  float* H, float* diag, float* sigma, float* H_scaled, float* lambda_out,
+                  void* ws, size_t ws_bytes, hipStream_t s) {
   const bool accumulate = flags & QZ_H_ACCUMULATE;
+  const bool finalize = !(flags & QZ_H_NO_FINALIZE);
+  const size_t vec = align256(static_cast<size_t>(d) * sizeof(float));
+  float* dg = nullptr;   // raw diagonal, contiguous (bf16 path)
+  float* sg = reinterpret_cast<float*>(static_cast<char*>(ws) + hessian_ws_bytes(n, d, xt) - vec);
   if (xt == QZ_BF16) {
     const HPlan p = plan_for(n, d);
-    if (p.n_tiles * p.S > 0x7fffffff) return fail(QZ_EINVAL, "hessian: d too large");
+    if (p.n_tiles * p.S > 0x7fffffff || p.n_tiles * (HT / RSB) * (HT / RSB) > 0x7fffffff)
+      return fail(QZ_EINVAL, "hessian: d too large");
     HArgs g;
     g.X = static_cast<const uint16_t*>(X);
     g.n = n;
@@ -504,6 +558,7 @@ int hessian_build(const void* X, int xt, int64_t n, int64_t d, float damp, uint3
     g.S = p.S;
     g.chunk = p.chunk;
     g.partial = reinterpret_cast<float*>(static_cast<char*>(ws) + p.tiles_bytes);
+    dg = reinterpret_cast<float*>(static_cast<char*>(ws) + p.tiles_bytes + p.partial_bytes);
     g.vec = (d % 8 == 0) && (reinterpret_cast<uintptr_t>(X) % 16 == 0);
     schedule_kernel<<<1, 64, 0, s>>>(p.T, const_cast<int32_t*>(g.tiles));
     QZ_TRY(check_launch("gram_schedule"));
@@ -516,13 +571,13 @@ int hessian_build(const void* X, int xt, int64_t n, int64_t d, float damp, uint3
       QZ_TRY(check_launch("gram_bf16"));
     }
     ScopedTimer tm(K_HESSIAN_FINISH, s);
-    const int64_t total = p.n_tiles * HT * HT;
-    const int nb = static_cast<int>(ceil_div(total, kSmall) > 65536 ? 65536 : ceil_div(total, kSmall));
-    gram_reduce_kernel<<<nb, kSmall, 0, s>>>(g.partial, p.S, p.n_tiles, g.tiles, d,
-                                             accumulate ? 1 : 0, H);
-    QZ_TRY(check_launch("gram_reduce"));
+    const int64_t per = (HT / RSB) * (HT / RSB);
+    reduce_mirror_kernel<<<static_cast<unsigned>(p.n_tiles * per), kSmall, 0, s>>>(
+        g.partial, p.S, p.n_tiles, g.tiles, d, accumulate ? 1 : 0, finalize ? 1 : 0, H, dg);
+    QZ_TRY(check_launch("gram_reduce_mirror"));
   } else {
-    // fp32 input: X^T staged K-contiguous, then the fp32 matrix-core GEMM.
+    // fp32 input: X^T staged K-contiguous, then the fp32 matrix-core GEMM over the full
+    // square; the mirror below makes it exactly symmetric.
     const int64_t ldt = round_up(n, 4);
     float* Xt = static_cast<float*>(ws);
     QZ_TRY(launch_transpose_f32(static_cast<const float*>(X), n, d, d, Xt, ldt, s));
@@ -534,14 +589,21 @@ int hessian_build(const void* X, int xt, int64_t n, int64_t d, float damp, uint3
     ScopedTimer tm(K_HESSIAN_GRAM, s);
     QZ_TRY(launch_gemm_nt(accumulate ? EPI_ADD : EPI_STORE, a, s));
   }
-  if (!(flags & QZ_H_NO_FINALIZE)) {
+  if (finalize) {
     ScopedTimer tm(K_HESSIAN_FINISH, s);
-    lambda_kernel<<<1, kSmall, 0, s>>>(H, d, damp, diag, sigma, lambda_out);
+    if (!dg) {
+      const int64_t nt = ceil_div(d, 32);
+      dim3 grid(static_cast<unsigned>(nt), static_cast<unsigned>(nt));
+      mirror_kernel<<<grid, kSmall, 0, s>>>(H, d);
+      QZ_TRY(check_launch("mirror"));
+    }
+    lambda_kernel<<<1, kLam, 0, s>>>(H, d, dg, damp, diag, sigma, lambda_out, sg);
     QZ_TRY(check_launch("lambda"));
-    const int64_t nt = ceil_div(d, 32);
-    dim3 grid(static_cast<unsigned>(nt), static_cast<unsigned>(nt));
-    mirror_kernel<<<grid, kSmall, 0, s>>>(H, d);
-    QZ_TRY(check_launch("mirror"));
+    if (H_scaled) {
+      const int64_t nb = d < 65536 ? d : 65536;
+      scaled_kernel<<<static_cast<unsigned>(nb), kSmall, 0, s>>>(H, d, sg, H_scaled);
+      QZ_TRY(check_launch("h_scaled"));
+    }
   }
   (void)ws_bytes;
   return QZ_OK;

@@ -191,8 +191,8 @@ int launch_ls_accept(const float* H, int64_t d_i, uint8_t* codes, const float* s
 // bf16 Hessian (k_hessian.hip)
 size_t hessian_ws_bytes(int64_t n, int64_t d, int xt);
 int hessian_build(const void* X, int xt, int64_t n, int64_t d, float damp, uint32_t flags,
-                  float* H, float* diag, float* sigma, float* lambda_out, void* ws,
-                  size_t ws_bytes, hipStream_t s);
+                  float* H, float* diag, float* sigma, float* H_scaled, float* lambda_out,
+                  void* ws, size_t ws_bytes, hipStream_t s);
 
 // orders and the error bound (k_order.hip)
 size_t order_ws_bytes(int64_t n, int kind);
@@ -252,7 +252,10 @@ int launch_range_of_grid(const float* scales, const uint8_t* zeros, int64_t n, i
                          float* lo0, float* hi0, hipStream_t s);
 int launch_copy_bytes(const void* src, int64_t n, void* dst, hipStream_t s);
 
-// eigen-decomposition (eig.cpp)
-int eig_scaled(const float* H, int64_t d, float* V, float* Lambda, float* sigma, hipStream_t s);
+// eigendecomposition of Sigma H Sigma (k_eig.hip): workspace bytes (asks the solver library
+// for its scratch size once per size), and the decomposition in the caller's workspace
+int eig_ws_bytes(int64_t d, size_t* bytes);
+int eig_scaled(const float* H, int64_t d, float* V, float* Lambda, float* sigma, void* ws,
+               size_t ws_bytes, hipStream_t s);
 
 }  // namespace qz

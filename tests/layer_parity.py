@@ -69,7 +69,7 @@ def gptq_rows(name, Hf, W_bits, rows, bits, group, B, W_dev=None):
     s_ref, z_ref = grid.fit_grid_f32(Wf, bits, group)
     np.testing.assert_array_equal(s_g, s_ref)
     np.testing.assert_array_equal(z_g, z_ref)
-    ref, adopted = gptq.gptq(None, Wf, s_ref, z_ref, bits, group, B, R=oracle_R(H64), hint=c_g)
+    ref, adopted = gptq.gptq(None, Wf, s_ref, z_ref, bits, group, R=oracle_R(H64), hint=c_g)
     f_gpu = objective.row_objective(H64, Wf, grid.dequant(c_g, s_g, z_g, group))
     f_ref = objective.row_objective(H64, Wf, grid.dequant(ref, s_ref, z_ref, group))
     report("gptq_rows", layer=name, rows=len(rows), adopted=adopted,
@@ -145,7 +145,7 @@ def admm_rows_trajectory(name, Hf, W_bits, rows, bits, group, iters, rho0, gamma
     f_gpu = objective.row_objective(H64, Wf, grid.dequant(c_g, s_g, z_g, group))
     f_ref = objective.row_objective(H64, Wf, grid.dequant(o["codes"], o["scale"], o["zero"], group))
     s0, z0 = grid.fit_grid_f32(Wf, bits, group)
-    cg, _ = gptq.gptq(H64, Wf, s0, z0, bits, group, B)
+    cg, _ = gptq.gptq(H64, Wf, s0, z0, bits, group)
     f_gptq = objective.row_objective(H64, Wf, grid.dequant(cg, s0, z0, group))
     report("admm_rows", layer=name, rows=len(rows), step_adopted=step_adopted,
            step_max_rel_dU=f"{worst_u:.2e}", run_adopted=o["adopted"], run_departs_at=depart,

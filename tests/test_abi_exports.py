@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_queries(lib):
-    assert lib.qz_abi_version() == 1
+    assert lib.qz_abi_version() == 2
     assert lib.qz_packed_words(11, 3) == 2
     assert lib.qz_packed_words(128, 3) == 12
     assert lib.qz_packed_words(5, 9) == -1
@@ -43,16 +43,19 @@ def test_version_and_queries(lib):
     assert lib.qz_admmq_workspace(64, 128, 128, 20) > 0
     assert lib.qz_admmq_workspace(64, 128, 100, 20) == 0      # group must divide d_i
     assert lib.qz_hessian_workspace(512, 128, 0) > 0
+    assert 0 < lib.qz_rtn_workspace(64, 128) <= 256
+    assert lib.qz_rtn_workspace(-1, 128) == 0
+    assert lib.qz_admmq_prepare_workspace(0) == 0
 
 
 def test_argument_errors_without_gpu(lib):
     from post_weight_quantization_05_amd import _lib
     g = _lib.QzGrid(C.sizeof(_lib.QzGrid), 3, 7, 0)
     # group does not divide d_i
-    assert lib.qz_rtn(None, 0, 4, 16, C.byref(g), None, None, None, None) == _lib.QZ_EINVAL
+    assert lib.qz_rtn(None, 0, 4, 16, C.byref(g), None, None, None, None, 0, None) == _lib.QZ_EINVAL
     assert b"group" in lib.qz_last_error()
     g = _lib.QzGrid(C.sizeof(_lib.QzGrid), 1, 4, 0)
-    assert lib.qz_rtn(None, 0, 4, 16, C.byref(g), None, None, None, None) == _lib.QZ_EINVAL
+    assert lib.qz_rtn(None, 0, 4, 16, C.byref(g), None, None, None, None, 0, None) == _lib.QZ_EINVAL
     g = _lib.QzGrid(C.sizeof(_lib.QzGrid), 3, 4, 0)
     assert lib.qz_gptq(None, None, 0, 4, 16, C.byref(g), 0, None, None, None, None, None, 0,
                        None) == _lib.QZ_EINVAL
@@ -64,9 +67,9 @@ def test_argument_errors_without_gpu(lib):
                         None, None, None, 0, None) == _lib.QZ_EINVAL
     assert b"rho0" in lib.qz_last_error()
     assert lib.qz_pack(None, 2, 3, 0, None, None) == _lib.QZ_EINVAL
-    assert lib.qz_build_hessian(None, 0, 10, 0, 0.01, 0, None, None, None, None, None, 0,
+    assert lib.qz_build_hessian(None, 0, 10, 0, 0.01, 0, None, None, None, None, None, None, 0,
                                 None) == _lib.QZ_EINVAL
-    assert lib.qz_build_hessian(None, 7, 10, 4, 0.01, 0, None, None, None, None, None, 0,
+    assert lib.qz_build_hessian(None, 7, 10, 4, 0.01, 0, None, None, None, None, None, None, 0,
                                 None) == _lib.QZ_EINVAL
 
 
@@ -84,8 +87,24 @@ def test_misaligned_workspace_is_rejected(lib):
                         C.c_void_p(4096 + 8), need, None) == _lib.QZ_EWORKSPACE
     need = lib.qz_hessian_workspace(64, 16, 0)
     assert need > 0
-    assert lib.qz_build_hessian(d, 0, 64, 16, 0.01, 0, d, None, None, None, C.c_void_p(4096 + 128),
-                                need, None) == _lib.QZ_EWORKSPACE
+    assert lib.qz_build_hessian(d, 0, 64, 16, 0.01, 0, d, None, None, None, None,
+                                C.c_void_p(4096 + 128), need, None) == _lib.QZ_EWORKSPACE
+    # H_scaled may not alias H, and needs a finalised H
+    assert lib.qz_build_hessian(d, 0, 64, 16, 0.01, 0, d, None, None, d, None, d, need,
+                                None) == _lib.QZ_EINVAL
+    assert lib.qz_build_hessian(d, 0, 64, 16, 0.01, _lib.QZ_H_NO_FINALIZE, d, None, None,
+                                C.c_void_p(8192), None, d, need, None) == _lib.QZ_EINVAL
+    # RTN's status word comes from the caller's workspace
+    need = lib.qz_rtn_workspace(4, 16)
+    assert lib.qz_rtn(d, 0, 4, 16, C.byref(g), d, d, d, None, need, None) == _lib.QZ_EWORKSPACE
+    assert lib.qz_rtn(d, 0, 4, 16, C.byref(g), d, d, d, d, need - 1, None) == _lib.QZ_EWORKSPACE
+    assert lib.qz_rtn(d, 0, 4, 16, C.byref(g), d, d, d, C.c_void_p(4096 + 4), need,
+                      None) == _lib.QZ_EWORKSPACE
+    # the eigendecomposition's workspace too (checked before any device call)
+    assert lib.qz_admmq_prepare(d, 16, d, d, d, None, 1 << 20, None) == _lib.QZ_EWORKSPACE
+    assert lib.qz_admmq_prepare(d, 16, d, d, d, C.c_void_p(4096 + 16), 1 << 20,
+                                None) == _lib.QZ_EWORKSPACE
+    assert b"aligned" in lib.qz_last_error()
 
 
 def test_objective_argument_errors(lib):

@@ -145,3 +145,26 @@ def test_admm_errors():
     with pytest.raises(q.QzError) as e:
         q.qz_admmq_prepare(to_dev(Hn))
     assert e.value.status == -3
+
+
+def test_admm_prepare_caller_workspace():
+    """The eigendecomposition works in the caller's workspace: the size query, a buffer
+    one byte short rejected, the exact size accepted and giving the same bytes, and two
+    sizes in turn (the solver handle is kept per thread and device)."""
+    q = qz()
+    import torch
+    for d in (96, 200):
+        X = qz_synth.calib_bf16(24, 4 * d, d, p_out=0.02, f_out=30.0)
+        H, _ = hessian.hessian(X, 0.01)
+        Hd = to_dev(H.astype(np.float32))
+        need = q.qz_admmq_prepare_workspace(d)
+        assert need >= 8 * d * d
+        short = torch.empty(need - 1, dtype=torch.uint8, device="cuda")
+        with pytest.raises(q.QzError) as e:
+            q.qz_admmq_prepare(Hd, ws=short)
+        assert e.value.status == -6
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        a = q.qz_admmq_prepare(Hd, ws=ws)
+        b = q.qz_admmq_prepare(Hd)
+        for x, y in zip(a, b):
+            np.testing.assert_array_equal(to_host(x), to_host(y))

@@ -31,7 +31,7 @@ def _run_pair(H, W, bits, group, B, order=None, caller=None):
         s_ref, z_ref = grid.fit_grid_f32(Wf, bits, group)
         np.testing.assert_array_equal(s, s_ref)
         np.testing.assert_array_equal(z, z_ref)
-    ref, adopted = gptq.gptq(Hf.astype(np.float64), Wf, s, z, bits, group, B, order=order,
+    ref, adopted = gptq.gptq(Hf.astype(np.float64), Wf, s, z, bits, group, order=order,
                              hint=codes)
     H64 = Hf.astype(np.float64)
     f_gpu = objective.objective(H64, Wf, grid.dequant(codes, s, z, group))

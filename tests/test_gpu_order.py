@@ -193,7 +193,7 @@ def test_gptq_noclip_matches_oracle(which, bits, group, d_o, d_i):
     s_ref, z_ref = grid.fit_grid_f32(W, bits, group)
     np.testing.assert_array_equal(s_h, s_ref)
     np.testing.assert_array_equal(z_h, z_ref)
-    ref, adopted = gptq.gptq(H64, W, s_ref, z_ref, bits, group, 32, order=perm, clip=False, hint=c)
+    ref, adopted = gptq.gptq(H64, W, s_ref, z_ref, bits, group, order=perm, clip=False, hint=c)
     np.testing.assert_array_equal(c, ref)
     assert adopted <= max(2, 1e-3 * c.size)
     off = float(np.mean((c < 0) | (c > (1 << bits) - 1)))
@@ -238,7 +238,7 @@ def test_noclip_full_layer_rows_within_bound():
     Wf = qz_synth.bf16_bits_to_f32(W[rows])
     c = to_host(codes)[rows].astype(np.int64)
     R = gptq.inverse_factor_lapack(H64[np.ix_(perm, perm)])
-    ref, adopted = gptq.gptq(None, Wf, to_host(s)[rows], to_host(zz)[rows], bits, group, B,
+    ref, adopted = gptq.gptq(None, Wf, to_host(s)[rows], to_host(zz)[rows], bits, group,
                              order=perm, clip=False, hint=c, R=R)
     off = float(np.mean((to_host(codes) < 0) | (to_host(codes) > (1 << bits) - 1)))
     report("gptq_noclip_full", f_noclip=f_tot, bound=b_tot, f_over_bound=f_tot / b_tot,

@@ -103,3 +103,42 @@ def test_empty_inputs():
     assert q.qz_pack(codes, 3).shape == (0, 2)
     c, s, z = q.qz_rtn(torch.empty((0, 16), dtype=torch.float32, device="cuda"), 3, 8)
     assert c.shape == (0, 16)
+
+
+def test_rtn_concurrent_streams_keep_their_own_status():
+    """Each call's status word lives in its own workspace: a non-finite weight on one
+    stream is reported there only, while clean calls on another stream, running at the
+    same time from another host thread, keep reporting success."""
+    import threading
+
+    import torch
+    q = qz()
+    good = to_dev(qz_synth.weights_bf16(31, 256, 512))
+    badh = qz_synth.bf16_bits_to_f32(qz_synth.weights_bf16(32, 256, 512))
+    badh[100, 7] = np.nan
+    bad = to_dev(badh)
+    ref, _, _ = q.qz_rtn(good, 3, 128)
+    ref = to_host(ref)
+    errors = {"good": [], "bad": []}
+
+    def run(W, key, n):
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            for _ in range(n):
+                try:
+                    c, _, _ = q.qz_rtn(W, 3, 128)
+                    if key == "good" and not np.array_equal(to_host(c), ref):
+                        errors[key].append("codes")
+                    if key == "bad":
+                        errors[key].append("no error")
+                except q.QzError as e:
+                    if key == "good" or e.status != -3:
+                        errors[key].append(str(e))
+
+    th = [threading.Thread(target=run, args=(good, "good", 30)),
+          threading.Thread(target=run, args=(bad, "bad", 30))]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    assert errors == {"good": [], "bad": []}

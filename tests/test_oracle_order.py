@@ -98,7 +98,7 @@ def test_no_clip_gptq_objective_within_bound(which):
         s, z = grid.fit_grid_f32(W, 2, group)
         perm = {"natural": np.arange(d), "act": order.act_order(H),
                 "min_pivot": order.min_pivot_order(H)[0]}[which]
-        codes, _ = gptq.gptq(H, W, s, z, 2, group, B=8, order=perm, clip=False)
+        codes, _ = gptq.gptq(H, W, s, z, 2, group, order=perm, clip=False)
         f = objective.row_objective(H, W, grid.dequant(codes, s, z, group))
         b = order.layer_bound(H, s, group, perm)
         assert np.all(f <= b * (1 + 1e-9))

@@ -77,7 +77,7 @@ def test_gptq_worked_example_compensation():
         if route == "plain":
             codes = gptq.gptq_plain(H, W, s, z, c["bits"], c["group"])
         else:
-            codes, _ = gptq.gptq(H, W, s, z, c["bits"], c["group"], B=2)
+            codes, _ = gptq.gptq(H, W, s, z, c["bits"], c["group"])
         np.testing.assert_array_equal(codes, c["codes_gptq"])
         q = grid.dequant(codes, s, z, 1)
         assert objective.objective(H, W, q) == pytest.approx(pr["cost_compensated"], rel=1e-6)
@@ -97,7 +97,7 @@ def test_gptq_worked_example_collinear_needs_damping():
     H, lam = hessian.hessian(X, c["damp"])
     W = np.array([g["printed"]["W_hat"]], np.float32)
     s = np.array(c["scale"], np.float32); z = np.array(c["zero"], np.uint8)
-    codes, _, E = gptq.gptq(H, W, s, z, c["bits"], c["group"], B=2, return_E=True)
+    codes, _, E = gptq.gptq(H, W, s, z, c["bits"], c["group"], return_E=True)
     np.testing.assert_array_equal(codes, c["codes_gptq"])
     np.testing.assert_array_equal(gptq.gptq_plain(H, W, s, z, c["bits"], c["group"]), c["codes_gptq"])
     # pre-round value of the second weight: 0.51 + 0.49 / 1.01
@@ -124,16 +124,51 @@ def test_inverse_factor_lapack_is_the_same_factor():
         gptq.inverse_factor_lapack(-np.eye(3))
 
 
+def blocked_gptq(H, W_hat, scale, zero, bits, group, B, order=None, clip=True):
+    """The tutorial's section 3 evaluation order of the same compensations: blocks of B
+    columns; a fixed column's compensation goes at once to the later columns of its own
+    block and, for the columns after the block, is collected and applied in one matrix
+    product when the block is done.  Written here only to check that the regrouping
+    leaves the codes unchanged."""
+    d_o, d_i = W_hat.shape
+    order = np.arange(d_i) if order is None else np.asarray(order)
+    R = gptq.inverse_factor(np.asarray(H, np.float64)[np.ix_(order, order)])
+    Wk = np.asarray(W_hat, np.float64)[:, order].copy()
+    codes = np.zeros((d_o, d_i), np.int64)
+    for a in range(0, d_i, B):
+        b = min(a + B, d_i)
+        Eb = np.zeros((d_o, b - a))
+        for j in range(a, b):
+            g = order[j] // group
+            sj, zj = np.asarray(scale, np.float64)[:, g], np.asarray(zero, np.float64)[:, g]
+            c, _, _ = grid.round_codes(Wk[:, j] / sj, zj, bits, clip)
+            codes[:, order[j]] = c
+            Eb[:, j - a] = (Wk[:, j] - sj * (c - zj)) / R[j, j]
+            Wk[:, j + 1:b] -= np.outer(Eb[:, j - a], R[j, j + 1:b])
+        Wk[:, b:] -= Eb @ R[a:b, b:]
+    return codes
+
+
+@pytest.mark.parametrize("clip", [True, False])
+def test_gptq_factor_route_equals_lagrange_route(clip):
+    rng = np.random.default_rng(11)
+    d_i, d_o, bits, group = 40, 12, 3, 8
+    _, H = spd(d_i, rng)
+    W, s, z = layer(d_o, d_i, bits, group, rng)
+    a, _ = gptq.gptq(H, W, s, z, bits, group, clip=clip)
+    b = gptq.gptq_plain(H, W, s, z, bits, group, clip=clip)
+    np.testing.assert_array_equal(a, b)
+
+
 @pytest.mark.parametrize("B", [1, 3, 16, 40])
 @pytest.mark.parametrize("clip", [True, False])
-def test_gptq_blocked_equals_lagrange_route(B, clip):
+def test_gptq_blocked_evaluation_gives_the_same_codes(B, clip):
     rng = np.random.default_rng(10 + B)
     d_i, d_o, bits, group = 40, 12, 3, 8
     _, H = spd(d_i, rng)
     W, s, z = layer(d_o, d_i, bits, group, rng)
-    a, _ = gptq.gptq(H, W, s, z, bits, group, B, clip=clip)
-    b = gptq.gptq_plain(H, W, s, z, bits, group, clip=clip)
-    np.testing.assert_array_equal(a, b)
+    a, _ = gptq.gptq(H, W, s, z, bits, group, clip=clip)
+    np.testing.assert_array_equal(blocked_gptq(H, W, s, z, bits, group, B, clip=clip), a)
 
 
 def test_gptq_block_size_invariance_and_order():
@@ -141,13 +176,14 @@ def test_gptq_block_size_invariance_and_order():
     d_i, d_o = 64, 16
     _, H = spd(d_i, rng)
     W, s, z = layer(d_o, d_i, 2, 16, rng)
-    ref, _ = gptq.gptq(H, W, s, z, 2, 16, 1)
+    ref, _ = gptq.gptq(H, W, s, z, 2, 16)
     for B in (7, 32, 64, 128):
-        np.testing.assert_array_equal(gptq.gptq(H, W, s, z, 2, 16, B)[0], ref)
+        np.testing.assert_array_equal(blocked_gptq(H, W, s, z, 2, 16, B), ref)
     perm = rng.permutation(d_i)
-    a, _ = gptq.gptq(H, W, s, z, 2, 16, 8, order=perm)
+    a, _ = gptq.gptq(H, W, s, z, 2, 16, order=perm)
     b = gptq.gptq_plain(H, W, s, z, 2, 16, order=perm)
     np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(blocked_gptq(H, W, s, z, 2, 16, 8, order=perm), a)
 
 
 def test_inverse_factor_is_upper_cholesky_of_inverse():
@@ -170,7 +206,7 @@ def test_gptq_objective_is_half_sum_E_squared(clip):
     d_i, d_o = 48, 10
     _, H = spd(d_i, rng)
     W, s, z = layer(d_o, d_i, 3, 16, rng)
-    codes, _, E = gptq.gptq(H, W, s, z, 3, 16, 16, clip=clip, return_E=True)
+    codes, _, E = gptq.gptq(H, W, s, z, 3, 16, clip=clip, return_E=True)
     q = grid.dequant(codes, s, z, 16)
     np.testing.assert_allclose(objective.row_objective(H, W, q), 0.5 * (E ** 2).sum(1), rtol=1e-9)
 
@@ -179,7 +215,7 @@ def test_gptq_diagonal_hessian_is_rtn():
     rng = np.random.default_rng(8)
     H = np.diag(rng.uniform(0.5, 3.0, 32))
     W, s, z = layer(6, 32, 3, 8, rng)
-    codes, _ = gptq.gptq(H, W, s, z, 3, 8, 8)
+    codes, _ = gptq.gptq(H, W, s, z, 3, 8)
     np.testing.assert_array_equal(codes, grid.rtn_f32(W, s, z, 3, 8))
 
 
@@ -197,7 +233,7 @@ def test_gptq_on_grid_input_is_fixed_point():
     W = grid.dequant(codes, s, z, group).astype(np.float32)
     s2, z2 = grid.fit_grid_f32(W, bits, group)
     np.testing.assert_array_equal(grid.rtn_f32(W, s2, z2, bits, group), codes)
-    got, _ = gptq.gptq(H, W, s2, z2, bits, group, 8)
+    got, _ = gptq.gptq(H, W, s2, z2, bits, group)
     np.testing.assert_array_equal(got, codes)
     assert objective.objective(H, W, grid.dequant(got, s2, z2, group)) < 1e-12
 
@@ -214,7 +250,7 @@ def test_babai_equals_back_to_front_gptq_200_cases():
         s = rng.uniform(0.01, 0.03, d)
         z = rng.integers(0, 4, d).astype(np.float64)
         order = np.arange(d)[::-1]
-        cg, _ = gptq.gptq(H, w[None, :], s[:, None].T, z[None, :], 2, 1, B=int(rng.integers(1, d + 1)),
+        cg, _ = gptq.gptq(H, w[None, :], s[:, None].T, z[None, :], 2, 1,
                           order=order, clip=False)
         cb = lattice.babai_row_cholesky(H, w, s, z) + 0
         # Babai's integers are offsets relative to code units (v includes z already)
@@ -260,7 +296,7 @@ def test_theorem5_bound_no_clip():
         s = rng.uniform(0.005, 0.03, d).astype(np.float32)
         z = rng.integers(0, 4, d).astype(np.uint8)
         order = rng.permutation(d) if rng.random() < 0.5 else np.arange(d)
-        codes, _, E = gptq.gptq(H, w[None, :], s[None, :], z[None, :], 2, 1, B=4, order=order,
+        codes, _, E = gptq.gptq(H, w[None, :], s[None, :], z[None, :], 2, 1, order=order,
                                 clip=False, return_E=True)
         e = w - grid.dequant(codes, s[None, :], z[None, :], 1)[0]
         err = e @ H @ e
@@ -288,7 +324,7 @@ def test_enumeration_bounds_solvers_from_below(bits, d):
     rng = np.random.default_rng(20 + d)
     for _ in range(3):
         H, W, s, z = _tiny(rng, d, bits)
-        cg, _ = gptq.gptq(H, W, s, z, bits, d, B=2)
+        cg, _ = gptq.gptq(H, W, s, z, bits, d)
         rtn = grid.rtn_f32(W, s, z, bits, d)
         out = admm.admm(H, W, bits, d, 30, 0.1, 1.3, refresh_every=0)
         for r in range(2):
