@@ -131,6 +131,16 @@ int qz_rtn(const void* W, int32_t wt, int64_t d_o, int64_t d_i, const qz_grid* g
            uint8_t* codes, float* scales, uint8_t* zeros, void* ws, size_t ws_bytes,
            hipStream_t stream);
 
+/* qz_rtn_noalloc: qz_rtn for callers that cannot allocate device memory or hand over a
+ * workspace (code under stream capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, results and errors as qz_rtn, without ws: the status
+ * word lives in a 256-byte array of static device memory that the library holds on
+ * each GPU it runs on until the process ends; the call allocates nothing.  The status
+ * word is the only scratch, so every size qz_rtn accepts fits.  All calls on one GPU
+ * share that word: calls that overlap on one GPU (other streams or threads) race on
+ * it, and one may miss or misreport the other's non-finite weight.  SYNC.        */
+int qz_rtn_noalloc(const void* W, int32_t wt, int64_t d_o, int64_t d_i, const qz_grid* grid,
+                   uint8_t* codes, float* scales, uint8_t* zeros, hipStream_t stream);
 
 /* ------------------------------------------------------------------- GPTQ --
  * qz_gptq: GPTQ tutorial, section 3 (Algorithm 1).  R is the upper Cholesky

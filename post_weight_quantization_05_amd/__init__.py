@@ -128,6 +128,26 @@ def qz_rtn(W, bits, group, scales=None, zeros=None, ws=None):
     return codes, scales, zeros
 
 
+def qz_rtn_noalloc(W, bits, group, scales=None, zeros=None, codes=None):
+    """qz_rtn without a workspace (the library's static per-GPU status word; calls that
+    overlap on one GPU race on it).  Outputs may be passed in so that nothing is
+    allocated here either."""
+    torch = _torch()
+    _dev(W, "W")
+    d_o, d_i = W.shape
+    caller = scales is not None
+    G = d_i // group if group > 0 and d_i % group == 0 else 0
+    if not caller:
+        scales = torch.empty((d_o, G), dtype=torch.float32, device=W.device)
+        zeros = torch.empty((d_o, G), dtype=torch.uint8, device=W.device)
+    if codes is None:
+        codes = torch.empty((d_o, d_i), dtype=torch.uint8, device=W.device)
+    g = _grid(bits, group, caller)
+    _check(lib().qz_rtn_noalloc(_ptr(W), _dtype_code(W), d_o, d_i, C.byref(g), _ptr(codes),
+                                _ptr(scales), _ptr(zeros), _stream()))
+    return codes, scales, zeros
+
+
 def qz_gptq_workspace(d_o, d_i, B) -> int:
     return lib().qz_gptq_workspace(d_o, d_i, B)
 

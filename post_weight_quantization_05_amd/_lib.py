@@ -25,6 +25,7 @@ STATUS_NAMES = {0: "QZ_OK", -1: "QZ_EINVAL", -2: "QZ_ENOTPD", -3: "QZ_ENONFINITE
 
 # every entry point declared in include/qz.h
 EXPORTS = ("qz_hessian_workspace", "qz_build_hessian", "qz_rtn_workspace", "qz_rtn",
+           "qz_rtn_noalloc",
            "qz_gptq_workspace", "qz_gptq",
            "qz_gptq_noclip", "qz_order_workspace", "qz_order", "qz_error_bound_workspace",
            "qz_error_bound",
@@ -59,6 +60,7 @@ _SIGS = {
     "qz_build_hessian": (C.c_int, [P, I32, I64, I64, F, U32, P, P, P, P, P, P, SZ, P]),
     "qz_rtn_workspace": (SZ, [I64, I64]),
     "qz_rtn": (C.c_int, [P, I32, I64, I64, C.POINTER(QzGrid), P, P, P, P, SZ, P]),
+    "qz_rtn_noalloc": (C.c_int, [P, I32, I64, I64, C.POINTER(QzGrid), P, P, P, P]),
     "qz_gptq_workspace": (SZ, [I64, I64, I32]),
     "qz_gptq": (C.c_int, [P, P, I32, I64, I64, C.POINTER(QzGrid), I32, P, P, P, P, P, SZ, P]),
     "qz_gptq_noclip": (C.c_int, [P, P, I32, I64, I64, C.POINTER(QzGrid), I32, P, P, P, P, P, SZ,

@@ -3,6 +3,7 @@
 // every step runs in the kernels of the k_*.hip translation units.
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "qz_internal.h"
@@ -46,6 +47,35 @@ int rtn_run(const void* W, int32_t wt, int64_t d_o, int64_t d_i, const qz_grid* 
   uint32_t h = 0;
   QZ_TRY(read_flag(flag, stream, &h));
   if (h & FLAG_NONFINITE) return fail(QZ_ENONFINITE, "rtn: non-finite weight");
+  return QZ_OK;
+}
+
+// Scratch of the allocation-free entry point (qz_rtn_noalloc): a file-scope device
+// array, one copy per GPU, held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the symbol); it uses
+// the device address that hipGetSymbolAddress returns, looked up once per device with
+// that device current and kept.
+constexpr size_t kNoAllocScratchBytes = 256;
+__device__ __align__(256) uint32_t scratch[kNoAllocScratchBytes / sizeof(uint32_t)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint32_t* g_scratch[kMaxDevices] = {};
+
+int noalloc_scratch(uint32_t** out) {
+  int dev = 0;
+  QZ_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(QZ_EHIP, "device index out of range");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(QZ_EHIP, std::string("no-alloc scratch: hipGetSymbolAddress failed: ") +
+                               hipGetErrorString(e));
+    g_scratch[dev] = static_cast<uint32_t*>(p);
+  }
+  *out = g_scratch[dev];
   return QZ_OK;
 }
 
@@ -175,6 +205,21 @@ int qz_rtn(const void* W, int32_t wt, int64_t d_o, int64_t d_i, const qz_grid* g
   if (!W || !codes || !scales || !zeros) return fail(QZ_EINVAL, "rtn: null pointer");
   set_error("");
   return rtn_run(W, wt, d_o, d_i, grid, codes, scales, zeros, static_cast<uint32_t*>(ws), stream);
+}
+
+int qz_rtn_noalloc(const void* W, int32_t wt, int64_t d_o, int64_t d_i, const qz_grid* grid,
+                   uint8_t* codes, float* scales, uint8_t* zeros, hipStream_t stream) {
+  if (!valid_dtype(wt)) return fail(QZ_EINVAL, "rtn_noalloc: bad dtype");
+  if (d_o < 0 || d_i < 1) return fail(QZ_EINVAL, "rtn_noalloc: need d_o >= 0 and d_i >= 1");
+  QZ_TRY(check_grid(grid, d_i));
+  // the scratch holds the status word only, so every size fits
+  static_assert(kNoAllocScratchBytes >= sizeof(uint32_t), "scratch holds the status word");
+  if (d_o == 0) return QZ_OK;
+  if (!W || !codes || !scales || !zeros) return fail(QZ_EINVAL, "rtn_noalloc: null pointer");
+  set_error("");
+  uint32_t* flag = nullptr;
+  QZ_TRY(noalloc_scratch(&flag));
+  return rtn_run(W, wt, d_o, d_i, grid, codes, scales, zeros, flag, stream);
 }
 
 // ------------------------------------------------------------------ GPTQ
