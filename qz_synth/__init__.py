@@ -174,15 +174,17 @@ WORKLOADS = {
 
 # ---------------------------------------------------------------- decoder block
 # One 8B-like decoder block quantized sub-layer by sub-layer: (name, input, d_i, d_o,
-# weight seed).  Inputs: x0 = calibration tokens; x_attn = v_proj's output with its 8
-# heads of 128 channels each repeated 4 times; x_mlp = o_proj's output; x_down =
-# up_proj's output.  q/k/v share x0's Hessian and gate/up share x_mlp's.
+# weight seed).  Inputs (the block's input hidden states are the calibration tokens,
+# 128 sequences of seq_len tokens): x_qkv = RMSNorm of the hidden states; x_attn = the
+# causal attention output of each sequence; x_mlp = RMSNorm of the hidden states plus
+# o_proj's output; x_down = silu(gate) * up.  q/k/v share x_qkv's Hessian and gate/up
+# share x_mlp's.  Only sizes and seeds live here; tests/block_driver.py evaluates it.
 BLOCK_8B = dict(
-    n=262144, d_model=4096, d_ff=12288, kv_heads=8, head_dim=128, q_heads=32,
+    n=262144, seq_len=2048, d_model=4096, d_ff=12288, kv_heads=8, head_dim=128, q_heads=32,
     calib_seed=6, p_out=0.01, f_out=30.0, damp=0.01, group=128, B=128,
     iters=100, rho0=0.05, gamma=1.05, refresh=1,
-    sublayers=[("q_proj", "x0", 4096, 4096, 11), ("k_proj", "x0", 4096, 1024, 12),
-               ("v_proj", "x0", 4096, 1024, 13), ("o_proj", "x_attn", 4096, 4096, 14),
+    sublayers=[("q_proj", "x_qkv", 4096, 4096, 11), ("k_proj", "x_qkv", 4096, 1024, 12),
+               ("v_proj", "x_qkv", 4096, 1024, 13), ("o_proj", "x_attn", 4096, 4096, 14),
                ("gate_proj", "x_mlp", 4096, 12288, 15), ("up_proj", "x_mlp", 4096, 12288, 16),
                ("down_proj", "x_down", 12288, 4096, 17)],
 )

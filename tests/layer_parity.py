@@ -145,7 +145,7 @@ def admm_rows_trajectory(name, Hf, W_bits, rows, bits, group, iters, rho0, gamma
     f_gpu = objective.row_objective(H64, Wf, grid.dequant(c_g, s_g, z_g, group))
     f_ref = objective.row_objective(H64, Wf, grid.dequant(o["codes"], o["scale"], o["zero"], group))
     s0, z0 = grid.fit_grid_f32(Wf, bits, group)
-    cg, _ = gptq.gptq(H64, Wf, s0, z0, bits, group)
+    cg, _ = gptq.gptq(None, Wf, s0, z0, bits, group, R=oracle_R(H64))
     f_gptq = objective.row_objective(H64, Wf, grid.dequant(cg, s0, z0, group))
     report("admm_rows", layer=name, rows=len(rows), step_adopted=step_adopted,
            step_max_rel_dU=f"{worst_u:.2e}", run_adopted=o["adopted"], run_departs_at=depart,
