@@ -304,6 +304,132 @@ __global__ __launch_bounds__(kThreads) void project_reg_kernel(const AdmmProj p,
   }
 }
 
+// Two groups of 128 columns per wavefront: the lower and upper 32 lanes each own one
+// group, four consecutive columns per lane (16-byte loads and stores of W~, U, M and
+// 4-byte code accesses, half as many memory instructions per byte as one group per
+// wavefront).  The refresh's min/max is a 32-lane reduction (the row reductions, then
+// row_bcast:15 into rows 1 and 3: lane 31 ends with the lower group's range and lane 63
+// with the upper's).  Arithmetic per element is the same as project_reg_kernel's.
+// Wavefronts: the launch keeps the one-group kernel's workgroup count (so the partial
+// slots per iteration do not depend on the path); each wavefront keeps one pair of groups
+// and strides over rows, about 1.5 rows per wavefront on the 12288-row layers (a third as
+// many wavefronts, three rows each, measured 10% slower).
+__device__ __forceinline__ void half_wave_minmax(float& lo, float& hi) {
+  minmax_step<0xB1>(lo, hi);         // quad_perm [1,0,3,2]
+  minmax_step<0x4E>(lo, hi);         // quad_perm [2,3,0,1]
+  minmax_step<0x141>(lo, hi);        // row_half_mirror
+  minmax_step<0x140>(lo, hi);        // row_mirror
+  minmax_step<0x142, 0xA>(lo, hi);   // row_bcast:15 into rows 1 and 3
+  const float lo_a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lo), 31));
+  const float hi_a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, hi), 31));
+  const float lo_b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lo), 63));
+  const float hi_b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, hi), 63));
+  const bool upper = (threadIdx.x & 63) >= 32;
+  lo = upper ? lo_b : lo_a;
+  hi = upper ? hi_b : hi_a;
+}
+
+__global__ __launch_bounds__(kThreads) void project_pair_kernel(const AdmmProj p,
+                                                                const float* __restrict__ inv_sigma) {
+  constexpr int EPL = 4;
+  __shared__ double red[kThreads / 64][2];
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int64_t G = p.d_i / p.group;
+  const int64_t G2 = G / 2;
+  const int64_t nw1 = proj_waves(G, p.d_o);
+  int64_t per = nw1 / G2;
+  if (per < 1) per = 1;
+  const int64_t nwaves = per * G2;
+  const int64_t w = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + wid;
+  const float maxq = static_cast<float>((1 << p.bits) - 1);
+  const float rs = p.rescale ? p.rho / p.rho_next : 1.0f;
+  float sum_p = 0.f, sum_d = 0.f;
+  if (w < nwaves) {
+    const int64_t gp = w % G2;
+    const int64_t gc = 2 * gp + (lane >> 5);
+    const int64_t cc = gp * 256 + lane * EPL;
+    float sg[EPL], isg[EPL];
+    vload<EPL>(p.sigma + cc, sg);
+    vload<EPL>(inv_sigma + cc, isg);
+    for (int64_t r = w / G2; r < p.d_o; r += per) {
+      const int64_t t = r * G + gc;
+      float wv[EPL], u[EPL];
+      uint8_t cd[EPL];
+      vload<EPL>(p.Wt + r * p.ldw + cc, wv);
+      vload<EPL>(p.U + r * p.d_i + cc, u);
+      cload<EPL>(p.codes + r * p.d_i + cc, cd);
+      const float s_old = p.scales[t];
+      const float z_old = static_cast<float>(p.zeros[t]);
+      float s = s_old, z = z_old;
+      if (p.refresh) {
+        float lo = 0.f, hi = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          float v = wv[e];
+          if (p.refresh == 3) v += u[e];
+          v *= sg[e];
+          lo = fminf(lo, v);
+          hi = fmaxf(hi, v);
+        }
+        half_wave_minmax(lo, hi);
+        if (hi == lo) { lo = -1.f; hi = 1.f; }
+        if (p.refresh != 2) {
+          lo = fmaxf(lo, p.lo0[t]);
+          hi = fminf(hi, p.hi0[t]);
+        }
+        if (hi > lo) {   // a range closed by the clamp keeps the current grid
+          s = (hi - lo) / maxq;
+          z = fminf(fmaxf(__builtin_rintf(-lo / s), 0.f), maxq);
+        }
+      }
+      const float rcp = 1.0f / s;
+      float un[EPL], mm[EPL];
+      uint8_t cn[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const float zv = (wv[e] + u[e]) * sg[e];
+        const float c = fminf(fmaxf(__builtin_rintf(zv * rcp) + z, 0.f), maxq);
+        const float dt = s * (c - z) * isg[e];
+        const float dold = s_old * (static_cast<float>(cd[e]) - z_old) * isg[e];
+        un[e] = (u[e] + wv[e] - dt) * rs;
+        mm[e] = dt - un[e];
+        cn[e] = static_cast<uint8_t>(c);
+        const float ep = wv[e] - dt, ed = dt - dold;
+        sum_p += ep * ep;
+        sum_d += ed * ed;
+      }
+      vstore<EPL>(p.U + r * p.d_i + cc, un);
+      vstore<EPL>(p.M + r * p.ldm + cc, mm);
+      cstore<EPL>(p.codes + r * p.d_i + cc, cn);
+      if (p.refresh && (lane & 31) == 0) {
+        p.scales[t] = s;
+        p.zeros[t] = static_cast<uint8_t>(z);
+      }
+    }
+  }
+  double acc_p = sum_p, acc_d = sum_d;
+  for (int off = 32; off > 0; off >>= 1) {
+    acc_p += __shfl_xor(acc_p, off);
+    acc_d += __shfl_xor(acc_d, off);
+  }
+  if (lane == 0) {
+    red[wid][0] = acc_p;
+    red[wid][1] = acc_d;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double sp = 0.0, sd = 0.0;
+    for (int k = 0; k < kThreads / 64; ++k) {
+      sp += red[k][0];
+      sd += red[k][1];
+    }
+    const double rho = p.rho;
+    p.partial[2 * blockIdx.x] = sp;
+    p.partial[2 * blockIdx.x + 1] = rho * rho * sd;
+  }
+}
+
 // M = s (C - z) / Sigma - U  (U may be null: zero)
 __global__ __launch_bounds__(kThreads) void init_m_kernel(const uint8_t* __restrict__ codes,
                                                           const float* __restrict__ scales,
@@ -422,7 +548,9 @@ int launch_admm_project(const AdmmProj& p, hipStream_t s, const float* inv_sigma
                   (reinterpret_cast<uintptr_t>(p.codes) % 4 == 0) &&
                   (reinterpret_cast<uintptr_t>(p.sigma) % 16 == 0);
   const int nb = admm_proj_blocks(p.d_i / p.group, p.d_o);
-  if (al && p.group == 128)
+  if (al && p.group == 128 && (p.d_i / p.group) % 2 == 0)
+    project_pair_kernel<<<nb, kThreads, 0, s>>>(p, inv_sigma);
+  else if (al && p.group == 128)
     project_reg_kernel<2><<<nb, kThreads, 0, s>>>(p, inv_sigma);
   else if (al && p.group == 256)
     project_reg_kernel<4><<<nb, kThreads, 0, s>>>(p, inv_sigma);

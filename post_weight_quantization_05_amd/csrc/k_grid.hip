@@ -101,20 +101,74 @@ __global__ __launch_bounds__(kThreads) void grid_fit_wave(
   }
 }
 
+// Eight consecutive columns of one row per thread (blockIdx.y strides over rows), so no
+// thread divides a flat index; the fast path loads the eight weights with one vector
+// load (bf16: 16 bytes; fp32: two 16-byte loads).
+constexpr int kPer = 8;
+
+template <int WT>
+__device__ __forceinline__ void load_row8(const void* __restrict__ W, int64_t off, int64_t n_left,
+                                          bool vec, float (&v)[kPer]) {
+  if (vec && n_left >= kPer) {
+    if constexpr (WT == QZ_BF16) {
+      const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(W) + off);
+      const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w4[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w4[i] & 0xffff0000u);
+      }
+    } else {
+      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(W) + off);
+      const float4 a = p[0], b = p[1];
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) v[i] = (i < n_left) ? load_w<WT>(W, off + i) : 0.f;
+}
+
+// vec: every row of W starts on a 16-byte boundary (so each 8-column chunk does too)
 template <int WT>
 __global__ __launch_bounds__(kThreads) void rtn_kernel(const void* __restrict__ W, int64_t rows,
                                                        int64_t cols, int group, float maxq,
                                                        const float* __restrict__ scales,
                                                        const uint8_t* __restrict__ zeros,
-                                                       uint8_t* __restrict__ codes) {
+                                                       uint8_t* __restrict__ codes, int vec) {
   const int64_t G = cols / group;
-  const int64_t total = rows * cols;
-  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t r = e / cols, c = e % cols;
-    const int64_t gi = r * G + c / group;
-    float x = load_w<WT>(W, e);
-    codes[e] = static_cast<uint8_t>(quant_code(x, scales[gi], static_cast<float>(zeros[gi]), maxq));
+  const int64_t c0 = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * kPer;
+  if (c0 >= cols) return;
+  const int64_t n_left = cols - c0;
+  const bool one_group = (group % kPer == 0);   // the eight columns share one group
+  const bool vstore = vec && n_left >= kPer && (cols % kPer == 0);
+  for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
+    float v[kPer];
+    load_row8<WT>(W, r * cols + c0, n_left, vec != 0, v);
+    uint8_t c[kPer];
+    if (one_group) {
+      const int64_t gi = r * G + c0 / group;
+      const float sc = scales[gi], z = static_cast<float>(zeros[gi]);
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) c[i] = static_cast<uint8_t>(quant_code(v[i], sc, z, maxq));
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int64_t gi = r * G + (c0 + i < cols ? c0 + i : cols - 1) / group;
+        c[i] = static_cast<uint8_t>(quant_code(v[i], scales[gi], static_cast<float>(zeros[gi]), maxq));
+      }
+    }
+    uint8_t* dst = codes + r * cols + c0;
+    if (vstore) {
+      uint2 w;
+      __builtin_memcpy(&w, c, sizeof(w));
+      *reinterpret_cast<uint2*>(dst) = w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        if (i < n_left) dst[i] = c[i];
+    }
   }
 }
 
@@ -164,19 +218,52 @@ __global__ __launch_bounds__(kThreads) void to_f32_kernel(const void* __restrict
                                                           int64_t cols, const int32_t* __restrict__ perm,
                                                           const float* __restrict__ div,
                                                           float* __restrict__ out, int64_t ldo,
-                                                          uint32_t* __restrict__ flag) {
-  const int64_t total = rows * cols;
+                                                          uint32_t* __restrict__ flag, int vec,
+                                                          int vout) {
+  const int64_t c0 = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * kPer;
   bool bad = false;
-  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t r = e / cols, j = e % cols;
-    const int64_t c = perm ? perm[j] : j;
-    float v = load_w<WT>(W, r * cols + c);
-    if (div) v = v / div[c];
-    bad |= !__builtin_isfinite(v);
-    out[r * ldo + j] = v;
+  if (c0 < cols) {
+    const int64_t n_left = cols - c0;
+    float dv[kPer];
+    if (div) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int64_t j = c0 + i < cols ? c0 + i : cols - 1;
+        dv[i] = div[perm ? perm[j] : j];
+      }
+    }
+    for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
+      float v[kPer];
+      if (perm) {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+          v[i] = (i < n_left) ? load_w<WT>(W, r * cols + perm[c0 + i]) : 0.f;
+      } else {
+        load_row8<WT>(W, r * cols + c0, n_left, vec != 0, v);
+      }
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        if (div) v[i] = v[i] / dv[i];
+        bad |= (i < n_left) && !__builtin_isfinite(v[i]);
+      }
+      float* dst = out + r * ldo + c0;
+      if (vout && n_left >= kPer) {
+        *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(v[4], v[5], v[6], v[7]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+          if (i < n_left) dst[i] = v[i];
+      }
+    }
   }
   if (flag && __any(bad) && (threadIdx.x & 63) == 0) atomicOr(flag, FLAG_NONFINITE);
+}
+
+inline dim3 row_grid(int64_t rows, int64_t cols) {
+  const int64_t gx = ceil_div(cols, static_cast<int64_t>(kThreads) * kPer);
+  const int64_t gy = rows < 65535 ? rows : 65535;
+  return dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy > 0 ? gy : 1));
 }
 
 __global__ __launch_bounds__(kThreads) void finite_kernel(const float* __restrict__ p, int64_t n,
@@ -289,13 +376,17 @@ int launch_grid_fit(const void* W, int wt, int64_t rows, int64_t cols, int group
 int launch_rtn(const void* W, int wt, int64_t rows, int64_t cols, int group, int bits,
                const float* scales, const uint8_t* zeros, uint8_t* codes, hipStream_t s) {
   const float maxq = static_cast<float>((1 << bits) - 1);
-  const int64_t n = rows * cols;
-  if (n == 0) return QZ_OK;
-  int nb = blocks_for(n, kThreads * 4, 65536);
+  if (rows * cols == 0) return QZ_OK;
+  const int64_t esz = (wt == QZ_BF16) ? 2 : 4;
+  // vector loads need every row start on a 16-byte boundary; the 8-byte code stores need
+  // 8-byte aligned row starts of `codes`
+  const int vec = ((cols * esz) % 16 == 0) && (reinterpret_cast<uintptr_t>(W) % 16 == 0) &&
+                  (reinterpret_cast<uintptr_t>(codes) % 8 == 0);
+  const dim3 grid = row_grid(rows, cols);
   if (wt == QZ_BF16)
-    rtn_kernel<QZ_BF16><<<nb, kThreads, 0, s>>>(W, rows, cols, group, maxq, scales, zeros, codes);
+    rtn_kernel<QZ_BF16><<<grid, kThreads, 0, s>>>(W, rows, cols, group, maxq, scales, zeros, codes, vec);
   else
-    rtn_kernel<QZ_F32><<<nb, kThreads, 0, s>>>(W, rows, cols, group, maxq, scales, zeros, codes);
+    rtn_kernel<QZ_F32><<<grid, kThreads, 0, s>>>(W, rows, cols, group, maxq, scales, zeros, codes, vec);
   return check_launch("rtn");
 }
 
@@ -319,13 +410,15 @@ int launch_unpack(const uint32_t* in, int64_t rows, int64_t cols, int bits, uint
 
 int launch_to_f32(const void* W, int wt, int64_t rows, int64_t cols, const int32_t* perm,
                   const float* div, float* out, int64_t ldo, uint32_t* flag, hipStream_t s) {
-  const int64_t n = rows * cols;
-  if (n == 0) return QZ_OK;
-  int nb = blocks_for(n, kThreads * 4, 65536);
+  if (rows * cols == 0) return QZ_OK;
+  const int64_t esz = (wt == QZ_BF16) ? 2 : 4;
+  const int vec = ((cols * esz) % 16 == 0) && (reinterpret_cast<uintptr_t>(W) % 16 == 0);
+  const int vout = (ldo % 4 == 0) && (reinterpret_cast<uintptr_t>(out) % 16 == 0);
+  const dim3 grid = row_grid(rows, cols);
   if (wt == QZ_BF16)
-    to_f32_kernel<QZ_BF16><<<nb, kThreads, 0, s>>>(W, rows, cols, perm, div, out, ldo, flag);
+    to_f32_kernel<QZ_BF16><<<grid, kThreads, 0, s>>>(W, rows, cols, perm, div, out, ldo, flag, vec, vout);
   else
-    to_f32_kernel<QZ_F32><<<nb, kThreads, 0, s>>>(W, rows, cols, perm, div, out, ldo, flag);
+    to_f32_kernel<QZ_F32><<<grid, kThreads, 0, s>>>(W, rows, cols, perm, div, out, ldo, flag, vec, vout);
   return check_launch("to_f32");
 }
 

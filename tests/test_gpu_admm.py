@@ -97,7 +97,8 @@ def test_admm_reading_variants(flags):
 
 @pytest.mark.parametrize("d_o,d_i,bits,group,refresh", [(70, 200, 3, 8, 1), (33, 256, 2, 128, 0),
                                                         (17, 96, 4, 1, 3), (9, 512, 3, 256, 1),
-                                                        (12, 192, 4, 64, 2), (21, 384, 3, 128, 1)])
+                                                        (12, 192, 4, 64, 2), (21, 384, 3, 128, 1),
+                                                        (19, 512, 3, 128, 3), (1, 256, 2, 128, 2)])
 def test_admm_ragged(d_o, d_i, bits, group, refresh):
     X = qz_synth.calib_bf16(22, 4 * d_i, d_i, p_out=0.02, f_out=30.0)
     H, _ = hessian.hessian(X, 0.01)
