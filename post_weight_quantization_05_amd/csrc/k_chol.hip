@@ -71,71 +71,224 @@ __device__ __forceinline__ double rsqrt_f64(double p) {
   return y;
 }
 
-// Factor diagonal block k in place (lower) and write its inverse to Dinv[k].
-// One wavefront: lane i holds row i of the block in registers during the factorisation
-// (all 64 loads of a row in flight at once).  Per column j the pivot is broadcast
-// from lane j (readlane) and every lane forms its reciprocal square root; the new
-// column goes to LDS twice, row-major (Ls, for the inverse) and column-major (Lc, so the
-// rank-one update of the rows below reads one contiguous run of uniform broadcasts).
-// The inverse is formed by forward substitution with lane i holding column i, each sum
-// split over four independent partial sums.
-__global__ __launch_bounds__(NB) void diag_block(double* __restrict__ A, int64_t lda, int64_t k,
-                                                 const double* __restrict__ diag0,
-                                                 double* __restrict__ Dinv,
-                                                 uint32_t* __restrict__ flag) {
-  __shared__ double Ls[NB][NB + 2];   // L row-major (even stride: 16-byte pair reads)
-  __shared__ double Lc[NB][NB];       // Lc[j][l] = L[l][j]
-  __shared__ double rinv[NB];
-  const int i = threadIdx.x;
-  const int64_t k0 = k * NB;
-  double a[NB];
-  const double* __restrict__ row = A + (k0 + i) * lda + k0;
-#pragma unroll
-  for (int c = 0; c < NB; ++c) a[c] = (c <= i) ? row[c] : 0.0;
-  const double tol = 1e-12 * diag0[k0 + i];
-  bool notpd = false;
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    const double p = readlane_f64(a[j], j);          // the pivot, uniform
-    if (i == j) notpd = !(p > tol) || !__builtin_isfinite(p);
-    const double r = rsqrt_f64(p > 0.0 ? p : 0.0);
-    if (i == 0) rinv[j] = r;
-    const double lij = (i >= j) ? a[j] * r : 0.0;
-    a[j] = lij;
-    Ls[i][j] = lij;
-    Lc[j][i] = lij;
-    // The block is one wavefront, whose LDS operations complete in issue order, so
-    // wavefront-scope ordering makes the column visible to every lane without waiting
-    // for the writes to finish before the reads are issued.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // a[i][l] -= L[i][j] L[l][j] for l > j.  Unguarded: lanes i < j have lij = 0, and the
-    // entries l > i it writes lie above the diagonal, which are never read as pivots or
-    // column entries (a[j] of lane i < j is replaced by lij = 0) nor stored.
-#pragma unroll
-    for (int l = j + 1; l < NB; ++l) a[l] = fma(-lij, Lc[j][l], a[l]);
+// Factor diagonal block k in place (lower) and write its inverse to Dinv[k]: four
+// wavefronts, the block held in LDS and factored right-looking over four 16-column panels:
+//   (1) every wavefront factors the panel's 16 x 16 diagonal sub-block and inverts it, the
+//       same work in each (so no workgroup barrier follows): the four lanes of a quad
+//       share a sub-block row, lane q keeping columns q, q+4, q+8, q+12 of it and of its
+//       inverse; per pivot j the pivot comes from its lane by readlane, the row's own
+//       column-j entry by a DPP quad broadcast, and column j of L and row j of the inverse
+//       go through the wavefront's own LDS slots (double-buffered by step parity, ordered
+//       at wavefront scope);
+//   (2) the rows below the sub-block: L[i][panel] = A[i][panel] (L_pp^{-1})^T, one quad
+//       per row, each row read and rewritten by the lanes of one quad only;
+//   (3) the trailing lower triangle: A[i][j] -= sum over the panel of L[i][m] L[j][m], in
+//       2 x 2 blocks; one barrier after (2) and one after (3).  Wavefront 0 writes L_pp
+//       into the block after the first of them, once every wavefront has read A_pp.
+// The inverse of the whole block then comes from block forward substitution over the
+// 16 x 16 blocks, whose diagonal blocks (1) already produced.  Entries above the diagonal
+// are never read as pivots or L entries and are not stored.
+constexpr int PB = 16;                  // panel width
+constexpr int kDiagThreads = 256;
+constexpr int LS = NB + 1;              // LDS row stride of the block (doubles)
+
+template <int Q>
+__device__ __forceinline__ double quad_bcast(double v) {
+  constexpr int ctrl = Q | (Q << 2) | (Q << 4) | (Q << 6);   // quad_perm [Q, Q, Q, Q]
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), ctrl, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), ctrl, 0xF, 0xF, false);
+  return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ double quad_bcast_n(double v, int q) {
+  switch (q) {
+    case 0: return quad_bcast<0>(v);
+    case 1: return quad_bcast<1>(v);
+    case 2: return quad_bcast<2>(v);
+    default: return quad_bcast<3>(v);
   }
-  if (notpd) atomicOr(flag, FLAG_NOTPD);
+}
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__global__ __launch_bounds__(kDiagThreads) void diag_block_panels(double* __restrict__ A, int64_t lda,
+                                                                  int64_t k,
+                                                                  const double* __restrict__ diag0,
+                                                                  double* __restrict__ Dinv,
+                                                                  uint32_t* __restrict__ flag) {
+  __shared__ double S[NB * LS];               // the block, then L (lower)
+  __shared__ double Xw[4][PB][PB + 1];        // per wavefront: the panel's L_pp^{-1}
+  __shared__ double cb[4][2][PB];             // per wavefront: column j of L_pp
+  __shared__ double xb[4][2][PB];             // per wavefront: row j of L_pp^{-1}
+  __shared__ double rinv[NB];                 // 1 / L[r][r]
+  __shared__ double tolv[NB];                 // 1e-12 of the original diagonal
+  __shared__ double Xf[NB * LS];              // X = L^{-1}: diagonal blocks from (1), then the rest
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int r = lane >> 2, q = lane & 3;
+  const int64_t k0 = k * NB;
+
+  // all 16 loads of a thread in flight at once (every address lies inside A; entries above
+  // the diagonal are replaced by zero afterwards)
+  {
+    constexpr int PER = NB * NB / kDiagThreads;
+    double v[PER];
 #pragma unroll
-  for (int c = 0; c < NB; ++c)
-    if (c <= i) A[(k0 + i) * lda + k0 + c] = a[c];
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  // Ls holds L (lower; entries above the diagonal are zero); rinv[r] = 1 / L[r][r]
-  // X = L^{-1}, lane i holds column i: x[r] = (delta_ri - sum_{q<r} L[r][q] x[q]) / L[r][r]
-  double x[NB];
+    for (int t = 0; t < PER; ++t) {
+      const int e = tid + t * kDiagThreads;
+      v[t] = A[(k0 + e / NB) * lda + k0 + e % NB];
+    }
+    if (tid < NB) tolv[tid] = 1e-12 * diag0[k0 + tid];
 #pragma unroll
-  for (int r = 0; r < NB; ++r) {
-    double acc[4] = {(r == i) ? 1.0 : 0.0, 0.0, 0.0, 0.0};
+    for (int t = 0; t < PER; ++t) {
+      const int e = tid + t * kDiagThreads;
+      const int i = e / NB, c = e % NB;
+      S[i * LS + c] = (c <= i) ? v[t] : 0.0;
+    }
+  }
+  __syncthreads();
+
+  bool notpd = false;
+#pragma unroll 1
+  for (int c0 = 0; c0 < NB; c0 += PB) {
+    // (1) the 16 x 16 diagonal sub-block, in every wavefront
+    double a[4], x[4];
 #pragma unroll
-    for (int q = 0; q < r; ++q) acc[q & 3] = fma(-Ls[r][q], x[q], acc[q & 3]);
-    x[r] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) * rinv[r];
+    for (int u = 0; u < 4; ++u) {
+      const int c = q + 4 * u;
+      a[u] = S[(c0 + r) * LS + c0 + c];
+      x[u] = (c == r) ? 1.0 : 0.0;
+    }
+    const double tolr = tolv[c0 + r];
+#pragma unroll
+    for (int j = 0; j < PB; ++j) {
+      const int ju = j >> 2, jq = j & 3, b = j & 1;
+      const double p = readlane_f64(a[ju], 4 * j + jq);   // pivot, uniform
+      notpd = notpd || ((r == j) && (!(p > tolr) || !__builtin_isfinite(p)));
+      const double rj = rsqrt_f64(p > 0.0 ? p : 0.0);
+      const double own = quad_bcast_n(a[ju], jq);           // A[r][j] of this row
+      const double lrj = (r >= j) ? own * rj : 0.0;         // L[r][j]
+      if (q == jq) cb[wave][b][r] = lrj;
+      if (r == j) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) xb[wave][b][q + 4 * u] = x[u] * rj;
+      }
+      if (wave == 0 && lane == 0) rinv[c0 + j] = rj;
+      wave_sync_lds();
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int l = q + 4 * u;
+        const double lc = cb[wave][b][l];   // L[l][j] (zero for l < j)
+        const double xr = xb[wave][b][l];   // X[j][l]
+        a[u] = (l == j) ? lrj : fma(-lrj, lc, a[u]);
+        x[u] = (r == j) ? xr : fma(-lrj, xr, x[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      Xw[wave][r][q + 4 * u] = x[u];
+      if (wave == 0) Xf[(c0 + r) * LS + c0 + q + 4 * u] = x[u];
+    }
+    wave_sync_lds();
+    // (2) the rows below: L[i][c0 + c] = sum_m A[i][c0 + m] X[c][m]
+    const int nrows = NB - c0 - PB;
+    const int bq = wave * 16 + r;
+    if (bq < nrows) {
+      const int i = c0 + PB + bq;
+      double srow[PB];
+#pragma unroll
+      for (int m = 0; m < PB; ++m) srow[m] = S[i * LS + c0 + m];
+      double out[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = q + 4 * u;
+        double acc = 0.0;
+#pragma unroll
+        for (int m = 0; m < PB; ++m) acc = fma(srow[m], Xw[wave][c][m], acc);
+        out[u] = acc;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) S[i * LS + c0 + q + 4 * u] = out[u];
+    }
+    __syncthreads();
+    // L_pp into the block: only now, when every wavefront has read the sub-block
+    if (wave == 0) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = q + 4 * u;
+        if (c <= r) S[(c0 + r) * LS + c0 + c] = a[u];
+      }
+    }
+    // (3) trailing lower triangle, 2 x 2 blocks
+    if (nrows > 0) {
+      const int nb = nrows / 2;
+      const int base = c0 + PB;
+      for (int t = tid; t < nb * nb; t += kDiagThreads) {
+        const int bi = t / nb, bj = t % nb;
+        if (bj > bi) continue;
+        const int i0 = base + 2 * bi, j0 = base + 2 * bj;
+        double s00 = 0.0, s01 = 0.0, s10 = 0.0, s11 = 0.0;
+#pragma unroll
+        for (int m = 0; m < PB; ++m) {
+          const double li0 = S[i0 * LS + c0 + m], li1 = S[(i0 + 1) * LS + c0 + m];
+          const double lj0 = S[j0 * LS + c0 + m], lj1 = S[(j0 + 1) * LS + c0 + m];
+          s00 = fma(li0, lj0, s00);
+          s01 = fma(li0, lj1, s01);
+          s10 = fma(li1, lj0, s10);
+          s11 = fma(li1, lj1, s11);
+        }
+        S[i0 * LS + j0] -= s00;
+        S[i0 * LS + j0 + 1] -= s01;
+        S[(i0 + 1) * LS + j0] -= s10;
+        S[(i0 + 1) * LS + j0 + 1] -= s11;
+      }
+    }
+    __syncthreads();
+  }
+  if (__any(notpd) && tid == 0) atomicOr(flag, FLAG_NOTPD);
+
+#pragma unroll
+  for (int t = 0; t < NB * NB / kDiagThreads; ++t) {
+    const int e = tid + t * kDiagThreads;
+    const int i = e / NB, c = e % NB;
+    if (c <= i) A[(k0 + i) * lda + k0 + c] = S[i * LS + c];
+  }
+
+  // X = L^{-1} by block forward substitution over the 16 x 16 blocks, the diagonal blocks
+  // being the panels' inverses: X_ip = -X_ii sum_{q=p}^{i-1} L_iq X_qp for p < i, one block
+  // row after the other (two barriers each); thread (a, b) owns entry (a, b) of every block.
+  {
+    __shared__ double Tb[3][PB][PB + 1];
+    const int ea = tid >> 4, eb = tid & 15;
+#pragma unroll 1
+    for (int bi = 1; bi < NB / PB; ++bi) {
+      for (int bp = 0; bp < bi; ++bp) {
+        double t = 0.0;
+        for (int bq = bp; bq < bi; ++bq)
+#pragma unroll
+          for (int m = 0; m < PB; ++m)
+            t = fma(S[(PB * bi + ea) * LS + PB * bq + m], Xf[(PB * bq + m) * LS + PB * bp + eb], t);
+        Tb[bp][ea][eb] = t;
+      }
+      __syncthreads();
+      for (int bp = 0; bp < bi; ++bp) {
+        double t = 0.0;
+#pragma unroll
+        for (int m = 0; m < PB; ++m) t = fma(Xf[(PB * bi + ea) * LS + PB * bi + m], Tb[bp][m][eb], t);
+        Xf[(PB * bi + ea) * LS + PB * bp + eb] = -t;
+      }
+      __syncthreads();
+    }
   }
   double* __restrict__ out = Dinv + k * NB * NB;
 #pragma unroll
-  for (int r = 0; r < NB; ++r) out[r * NB + i] = (r >= i) ? x[r] : 0.0;
+  for (int t = 0; t < NB * NB / kDiagThreads; ++t) {
+    const int e = tid + t * kDiagThreads;
+    const int rr = e / NB, cc = e % NB;
+    out[e] = (rr >= cc) ? Xf[rr * LS + cc] : 0.0;
+  }
 }
 
 // Rows below block k:  A[i][k-block] <- A[i][k-block] * Dinv_k^T.  One 64-row tile
@@ -156,7 +309,9 @@ __device__ __forceinline__ void tri_tile(int64_t t, int64_t& ti, int64_t& tj) {
 //  A_op[m][q] = A[(am0 + m) * lda + ak0 + q]
 //  B_op[q][n] = BNN ? B[(bk0 + q) * ldb + bn0 + n] : B[(bn0 + n) * ldb + bk0 + q]
 // Both operands are staged in LDS before any output is written, so C may alias them.
-// Threads own 4 x 4 outputs (rows ty + 16a, cols tx + 16b).
+// Every thread issues all of its operand loads (and, when updating, its 16 loads of C)
+// before waiting for any of them.  Threads own 4 x 4 outputs (rows ty + 16a, cols
+// tx + 16b).
 template <bool BNN, bool STORE = false>
 __device__ __forceinline__ void tile_update(double* __restrict__ C, int64_t ldc, int64_t cm0,
                                             int64_t cn0, const double* __restrict__ A, int64_t lda,
@@ -164,15 +319,32 @@ __device__ __forceinline__ void tile_update(double* __restrict__ C, int64_t ldc,
                                             int64_t ldb, int64_t bk0, int64_t bn0) {
   __shared__ double as[NB][NB + 1];   // [q][m]
   __shared__ double bs[NB][NB + 1];   // [q][n]
+  constexpr int PER = NB * NB / kThreads;
   const int tid = threadIdx.x;
-  for (int e = tid; e < NB * NB; e += kThreads) {
+  const int tx = tid & 15, ty = tid >> 4;
+  double va[PER], vb[PER], cv[4][4];
+#pragma unroll
+  for (int t = 0; t < PER; ++t) {
+    const int e = tid + t * kThreads;
     const int r = e / NB, c = e % NB;
-    as[c][r] = A[(am0 + r) * lda + ak0 + c];              // A row r, k = c
-    if (BNN) bs[r][c] = B[(bk0 + r) * ldb + bn0 + c];     // k = r, n = c
-    else bs[c][r] = B[(bn0 + r) * ldb + bk0 + c];         // n = r, k = c
+    va[t] = A[(am0 + r) * lda + ak0 + c];                                       // A row r, k = c
+    vb[t] = BNN ? B[(bk0 + r) * ldb + bn0 + c] : B[(bn0 + r) * ldb + bk0 + c];   // (k, n) = (r, c) or (c, r)
+  }
+  if (!STORE) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) cv[a][b] = C[(cm0 + ty + 16 * a) * ldc + cn0 + tx + 16 * b];
+  }
+#pragma unroll
+  for (int t = 0; t < PER; ++t) {
+    const int e = tid + t * kThreads;
+    const int r = e / NB, c = e % NB;
+    as[c][r] = va[t];
+    if (BNN) bs[r][c] = vb[t];
+    else bs[c][r] = vb[t];
   }
   __syncthreads();
-  const int tx = tid & 15, ty = tid >> 4;
   double acc[4][4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
@@ -194,10 +366,7 @@ __device__ __forceinline__ void tile_update(double* __restrict__ C, int64_t ldc,
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       double* c = C + (cm0 + ty + 16 * a) * ldc + cn0 + tx + 16 * b;
-      if (STORE)
-        *c = acc[a][b];
-      else
-        *c -= acc[a][b];
+      *c = STORE ? acc[a][b] : cv[a][b] - acc[a][b];
     }
 }
 
@@ -347,7 +516,7 @@ int factor_reversed(const float* H, int64_t d, const int32_t* perm, double* A, i
   }
   for (int64_t k = 0; k < nblk; ++k) {
     const int64_t below = nblk - k - 1;
-    diag_block<<<1, NB, 0, s>>>(A, dp, k, diag0, Dinv, flag);
+    diag_block_panels<<<1, kDiagThreads, 0, s>>>(A, dp, k, diag0, Dinv, flag);
     QZ_TRY(check_launch("rfactor.diag"));
     if (below > 0) {
       panel_solve<<<static_cast<unsigned>(below), kThreads, 0, s>>>(A, dp, k, Dinv);
