@@ -73,21 +73,19 @@ __device__ __forceinline__ double rsqrt_f64(double p) {
 
 // Factor diagonal block k in place (lower) and write its inverse to Dinv[k]: four
 // wavefronts, the block held in LDS and factored right-looking over four 16-column panels:
-//   (1) every wavefront factors the panel's 16 x 16 diagonal sub-block and inverts it, the
-//       same work in each (so no workgroup barrier follows): the four lanes of a quad
-//       share a sub-block row, lane q keeping columns q, q+4, q+8, q+12 of it and of its
-//       inverse; per pivot j the pivot comes from its lane by readlane, the row's own
-//       column-j entry by a DPP quad broadcast, and column j of L and row j of the inverse
-//       go through the wavefront's own LDS slots (double-buffered by step parity, ordered
-//       at wavefront scope);
-//   (2) the rows below the sub-block: L[i][panel] = A[i][panel] (L_pp^{-1})^T, one quad
-//       per row, each row read and rewritten by the lanes of one quad only;
-//   (3) the trailing lower triangle: A[i][j] -= sum over the panel of L[i][m] L[j][m], in
-//       2 x 2 blocks; one barrier after (2) and one after (3).  Wavefront 0 writes L_pp
-//       into the block after the first of them, once every wavefront has read A_pp.
-// The inverse of the whole block then comes from block forward substitution over the
-// 16 x 16 blocks, whose diagonal blocks (1) already produced.  Entries above the diagonal
-// are never read as pivots or L entries and are not stored.
+//   (1) wavefront 0 factors the panel's 16 x 16 diagonal sub-block: the four lanes of a
+//       quad share a sub-block row, lane q keeping columns q, q+4, q+8, q+12; per pivot j
+//       the pivot comes from its lane by readlane, the row's own column-j entry by a DPP
+//       quad broadcast, and the column entries L[l][j] the lane needs by ds_bpermute from
+//       the lanes of row l (no LDS round trip on the pivot chain);
+//   (2) wavefront 0 then solves the rows below against it, one lane per row holding the
+//       row's 16 entries (L[i][c] = (A[i][c] - sum_{m<c} L[i][m] L[c][m]) / L[c][c]);
+//   (3) all four wavefronts update the trailing lower triangle, A[i][j] -= sum over the
+//       panel of L[i][m] L[j][m], in 2 x 2 blocks; one barrier before (3), one after.
+// The inverse: each wavefront inverts one 16 x 16 diagonal block of L by forward
+// substitution (one lane per column), then block forward substitution fills the blocks
+// below the diagonal.  Entries above the diagonal are never read as pivots or L entries
+// and are not stored.
 constexpr int PB = 16;                  // panel width
 constexpr int kDiagThreads = 256;
 constexpr int LS = NB + 1;              // LDS row stride of the block (doubles)
@@ -107,6 +105,12 @@ __device__ __forceinline__ double quad_bcast_n(double v, int q) {
     default: return quad_bcast<3>(v);
   }
 }
+// v of lane `src` (ds_bpermute: a crossbar read, no LDS memory)
+__device__ __forceinline__ double lane_read(double v, int src) {
+  const int lo = __builtin_amdgcn_ds_bpermute(src * 4, __double2loint(v));
+  const int hi = __builtin_amdgcn_ds_bpermute(src * 4, __double2hiint(v));
+  return __hiloint2double(hi, lo);
+}
 __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -119,12 +123,9 @@ __global__ __launch_bounds__(kDiagThreads) void diag_block_panels(double* __rest
                                                                   double* __restrict__ Dinv,
                                                                   uint32_t* __restrict__ flag) {
   __shared__ double S[NB * LS];               // the block, then L (lower)
-  __shared__ double Xw[4][PB][PB + 1];        // per wavefront: the panel's L_pp^{-1}
-  __shared__ double cb[4][2][PB];             // per wavefront: column j of L_pp
-  __shared__ double xb[4][2][PB];             // per wavefront: row j of L_pp^{-1}
+  __shared__ double Xf[NB * LS];              // X = L^{-1}
   __shared__ double rinv[NB];                 // 1 / L[r][r]
   __shared__ double tolv[NB];                 // 1e-12 of the original diagonal
-  __shared__ double Xf[NB * LS];              // X = L^{-1}: diagonal blocks from (1), then the rest
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int r = lane >> 2, q = lane & 3;
@@ -153,74 +154,53 @@ __global__ __launch_bounds__(kDiagThreads) void diag_block_panels(double* __rest
   bool notpd = false;
 #pragma unroll 1
   for (int c0 = 0; c0 < NB; c0 += PB) {
-    // (1) the 16 x 16 diagonal sub-block, in every wavefront
-    double a[4], x[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int c = q + 4 * u;
-      a[u] = S[(c0 + r) * LS + c0 + c];
-      x[u] = (c == r) ? 1.0 : 0.0;
-    }
-    const double tolr = tolv[c0 + r];
-#pragma unroll
-    for (int j = 0; j < PB; ++j) {
-      const int ju = j >> 2, jq = j & 3, b = j & 1;
-      const double p = readlane_f64(a[ju], 4 * j + jq);   // pivot, uniform
-      notpd = notpd || ((r == j) && (!(p > tolr) || !__builtin_isfinite(p)));
-      const double rj = rsqrt_f64(p > 0.0 ? p : 0.0);
-      const double own = quad_bcast_n(a[ju], jq);           // A[r][j] of this row
-      const double lrj = (r >= j) ? own * rj : 0.0;         // L[r][j]
-      if (q == jq) cb[wave][b][r] = lrj;
-      if (r == j) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) xb[wave][b][q + 4 * u] = x[u] * rj;
-      }
-      if (wave == 0 && lane == 0) rinv[c0 + j] = rj;
-      wave_sync_lds();
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int l = q + 4 * u;
-        const double lc = cb[wave][b][l];   // L[l][j] (zero for l < j)
-        const double xr = xb[wave][b][l];   // X[j][l]
-        a[u] = (l == j) ? lrj : fma(-lrj, lc, a[u]);
-        x[u] = (r == j) ? xr : fma(-lrj, xr, x[u]);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      Xw[wave][r][q + 4 * u] = x[u];
-      if (wave == 0) Xf[(c0 + r) * LS + c0 + q + 4 * u] = x[u];
-    }
-    wave_sync_lds();
-    // (2) the rows below: L[i][c0 + c] = sum_m A[i][c0 + m] X[c][m]
     const int nrows = NB - c0 - PB;
-    const int bq = wave * 16 + r;
-    if (bq < nrows) {
-      const int i = c0 + PB + bq;
-      double srow[PB];
+    if (wave == 0) {
+      // (1) the 16 x 16 diagonal sub-block
+      double a[4];
 #pragma unroll
-      for (int m = 0; m < PB; ++m) srow[m] = S[i * LS + c0 + m];
-      double out[4];
+      for (int u = 0; u < 4; ++u) a[u] = S[(c0 + r) * LS + c0 + q + 4 * u];
+      const double tolr = tolv[c0 + r];
+#pragma unroll
+      for (int j = 0; j < PB; ++j) {
+        const int ju = j >> 2, jq = j & 3;
+        const double p = readlane_f64(a[ju], 4 * j + jq);   // pivot, uniform
+        notpd = notpd || ((r == j) && (!(p > tolr) || !__builtin_isfinite(p)));
+        const double rj = rsqrt_f64(p > 0.0 ? p : 0.0);
+        const double own = quad_bcast_n(a[ju], jq);           // A[r][j] of this row
+        const double lrj = (r >= j) ? own * rj : 0.0;         // L[r][j]
+        if (lane == 0) rinv[c0 + j] = rj;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int l = q + 4 * u;
+          const double lc = lane_read(lrj, 4 * l);   // L[l][j] (zero for l < j)
+          a[u] = (l == j) ? lrj : fma(-lrj, lc, a[u]);
+        }
+      }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int c = q + 4 * u;
-        double acc = 0.0;
-#pragma unroll
-        for (int m = 0; m < PB; ++m) acc = fma(srow[m], Xw[wave][c][m], acc);
-        out[u] = acc;
+        S[(c0 + r) * LS + c0 + c] = (c <= r) ? a[u] : 0.0;
       }
+      wave_sync_lds();
+      // (2) the rows below, one lane per row
+      if (lane < nrows) {
+        const int i = c0 + PB + lane;
+        double v[PB];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) S[i * LS + c0 + q + 4 * u] = out[u];
+        for (int m = 0; m < PB; ++m) v[m] = S[i * LS + c0 + m];
+#pragma unroll
+        for (int c = 0; c < PB; ++c) {
+          double acc = v[c];
+#pragma unroll
+          for (int m = 0; m < c; ++m) acc = fma(-v[m], S[(c0 + c) * LS + c0 + m], acc);
+          v[c] = acc * rinv[c0 + c];
+        }
+#pragma unroll
+        for (int m = 0; m < PB; ++m) S[i * LS + c0 + m] = v[m];
+      }
     }
     __syncthreads();
-    // L_pp into the block: only now, when every wavefront has read the sub-block
-    if (wave == 0) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int c = q + 4 * u;
-        if (c <= r) S[(c0 + r) * LS + c0 + c] = a[u];
-      }
-    }
     // (3) trailing lower triangle, 2 x 2 blocks
     if (nrows > 0) {
       const int nb = nrows / 2;
@@ -256,28 +236,54 @@ __global__ __launch_bounds__(kDiagThreads) void diag_block_panels(double* __rest
     if (c <= i) A[(k0 + i) * lda + k0 + c] = S[i * LS + c];
   }
 
-  // X = L^{-1} by block forward substitution over the 16 x 16 blocks, the diagonal blocks
-  // being the panels' inverses: X_ip = -X_ii sum_{q=p}^{i-1} L_iq X_qp for p < i, one block
-  // row after the other (two barriers each); thread (a, b) owns entry (a, b) of every block.
+  // X = L^{-1}.  Diagonal blocks: wavefront w inverts block w, lane c < 16 forming column c
+  // by forward substitution, x[r] = (delta_rc - sum_{c<=m<r} L[r][m] x[m]) / L[r][r].
+  {
+    const int b0 = PB * wave;
+    if (lane < PB) {
+      double x[PB];
+#pragma unroll
+      for (int rr = 0; rr < PB; ++rr) {
+        double acc = (rr == lane) ? 1.0 : 0.0;
+#pragma unroll
+        for (int m = 0; m < rr; ++m) acc = fma(-S[(b0 + rr) * LS + b0 + m], x[m], acc);
+        x[rr] = (rr >= lane) ? acc * rinv[b0 + rr] : 0.0;
+      }
+#pragma unroll
+      for (int rr = 0; rr < PB; ++rr) Xf[(b0 + rr) * LS + b0 + lane] = x[rr];
+    }
+  }
+  __syncthreads();
+  // blocks below the diagonal by block forward substitution: X_ip = -X_ii sum_{q=p}^{i-1}
+  // L_iq X_qp for p < i, one block row after the other (two barriers each); thread (a, b)
+  // owns entry (a, b) of every block
   {
     __shared__ double Tb[3][PB][PB + 1];
     const int ea = tid >> 4, eb = tid & 15;
-#pragma unroll 1
+#pragma unroll
     for (int bi = 1; bi < NB / PB; ++bi) {
+#pragma unroll
       for (int bp = 0; bp < bi; ++bp) {
-        double t = 0.0;
+        double t0 = 0.0, t1 = 0.0;
+#pragma unroll
         for (int bq = bp; bq < bi; ++bq)
 #pragma unroll
-          for (int m = 0; m < PB; ++m)
-            t = fma(S[(PB * bi + ea) * LS + PB * bq + m], Xf[(PB * bq + m) * LS + PB * bp + eb], t);
-        Tb[bp][ea][eb] = t;
+          for (int m = 0; m < PB; m += 2) {
+            t0 = fma(S[(PB * bi + ea) * LS + PB * bq + m], Xf[(PB * bq + m) * LS + PB * bp + eb], t0);
+            t1 = fma(S[(PB * bi + ea) * LS + PB * bq + m + 1], Xf[(PB * bq + m + 1) * LS + PB * bp + eb], t1);
+          }
+        Tb[bp][ea][eb] = t0 + t1;
       }
       __syncthreads();
-      for (int bp = 0; bp < bi; ++bp) {
-        double t = 0.0;
 #pragma unroll
-        for (int m = 0; m < PB; ++m) t = fma(Xf[(PB * bi + ea) * LS + PB * bi + m], Tb[bp][m][eb], t);
-        Xf[(PB * bi + ea) * LS + PB * bp + eb] = -t;
+      for (int bp = 0; bp < bi; ++bp) {
+        double t0 = 0.0, t1 = 0.0;
+#pragma unroll
+        for (int m = 0; m < PB; m += 2) {
+          t0 = fma(Xf[(PB * bi + ea) * LS + PB * bi + m], Tb[bp][m][eb], t0);
+          t1 = fma(Xf[(PB * bi + ea) * LS + PB * bi + m + 1], Tb[bp][m + 1][eb], t1);
+        }
+        Xf[(PB * bi + ea) * LS + PB * bp + eb] = -(t0 + t1);
       }
       __syncthreads();
     }
