@@ -117,15 +117,19 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__global__ __launch_bounds__(kDiagThreads) void diag_block_panels(double* __restrict__ A, int64_t lda,
-                                                                  int64_t k,
-                                                                  const double* __restrict__ diag0,
-                                                                  double* __restrict__ Dinv,
-                                                                  uint32_t* __restrict__ flag) {
-  __shared__ double S[NB * LS];               // the block, then L (lower)
-  __shared__ double Xf[NB * LS];              // X = L^{-1}
-  __shared__ double rinv[NB];                 // 1 / L[r][r]
-  __shared__ double tolv[NB];                 // 1e-12 of the original diagonal
+// LDS of factor_diag, in doubles: the block (then L), X = L^{-1}, 1 / L[r][r], the pivot
+// tolerances and three 16 x 16 staging blocks of the block substitution.
+constexpr int kDiagLds = 2 * NB * LS + 2 * NB + 3 * PB * (PB + 1);
+
+__device__ __forceinline__ void factor_diag(double* __restrict__ A, int64_t lda, int64_t k,
+                                            const double* __restrict__ diag0,
+                                            double* __restrict__ Dinv, uint32_t* __restrict__ flag,
+                                            double* smem) {
+  double* S = smem;                           // the block, then L (lower)
+  double* Xf = S + NB * LS;                   // X = L^{-1}
+  double* rinv = Xf + NB * LS;                // 1 / L[r][r]
+  double* tolv = rinv + NB;                   // 1e-12 of the original diagonal
+  double* Tb = tolv + NB;                     // [3][PB][PB + 1]
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int r = lane >> 2, q = lane & 3;
@@ -258,7 +262,6 @@ __global__ __launch_bounds__(kDiagThreads) void diag_block_panels(double* __rest
   // L_iq X_qp for p < i, one block row after the other (two barriers each); thread (a, b)
   // owns entry (a, b) of every block
   {
-    __shared__ double Tb[3][PB][PB + 1];
     const int ea = tid >> 4, eb = tid & 15;
 #pragma unroll
     for (int bi = 1; bi < NB / PB; ++bi) {
@@ -272,7 +275,7 @@ __global__ __launch_bounds__(kDiagThreads) void diag_block_panels(double* __rest
             t0 = fma(S[(PB * bi + ea) * LS + PB * bq + m], Xf[(PB * bq + m) * LS + PB * bp + eb], t0);
             t1 = fma(S[(PB * bi + ea) * LS + PB * bq + m + 1], Xf[(PB * bq + m + 1) * LS + PB * bp + eb], t1);
           }
-        Tb[bp][ea][eb] = t0 + t1;
+        Tb[(bp * PB + ea) * (PB + 1) + eb] = t0 + t1;
       }
       __syncthreads();
 #pragma unroll
@@ -280,8 +283,8 @@ __global__ __launch_bounds__(kDiagThreads) void diag_block_panels(double* __rest
         double t0 = 0.0, t1 = 0.0;
 #pragma unroll
         for (int m = 0; m < PB; m += 2) {
-          t0 = fma(Xf[(PB * bi + ea) * LS + PB * bi + m], Tb[bp][m][eb], t0);
-          t1 = fma(Xf[(PB * bi + ea) * LS + PB * bi + m + 1], Tb[bp][m + 1][eb], t1);
+          t0 = fma(Xf[(PB * bi + ea) * LS + PB * bi + m], Tb[(bp * PB + m) * (PB + 1) + eb], t0);
+          t1 = fma(Xf[(PB * bi + ea) * LS + PB * bi + m + 1], Tb[(bp * PB + m + 1) * (PB + 1) + eb], t1);
         }
         Xf[(PB * bi + ea) * LS + PB * bp + eb] = -(t0 + t1);
       }
@@ -297,10 +300,15 @@ __global__ __launch_bounds__(kDiagThreads) void diag_block_panels(double* __rest
   }
 }
 
-// Rows below block k:  A[i][k-block] <- A[i][k-block] * Dinv_k^T.  One 64-row tile
-// per workgroup.
-__global__ __launch_bounds__(kThreads) void panel_solve(double* __restrict__ A, int64_t lda, int64_t k,
-                                                        const double* __restrict__ Dinv);
+__global__ __launch_bounds__(kDiagThreads) void diag_block_panels(double* __restrict__ A, int64_t lda,
+                                                                  int64_t k,
+                                                                  const double* __restrict__ diag0,
+                                                                  double* __restrict__ Dinv,
+                                                                  uint32_t* __restrict__ flag) {
+  __shared__ double smem[kDiagLds];
+  factor_diag(A, lda, k, diag0, Dinv, flag, smem);
+}
+
 
 __device__ __forceinline__ void tri_tile(int64_t t, int64_t& ti, int64_t& tj) {
   // lower-triangle enumeration: (0,0), (1,0), (1,1), (2,0), ...
@@ -319,12 +327,14 @@ __device__ __forceinline__ void tri_tile(int64_t t, int64_t& ti, int64_t& tj) {
 // before waiting for any of them.  Threads own 4 x 4 outputs (rows ty + 16a, cols
 // tx + 16b).
 template <bool BNN, bool STORE = false>
-__device__ __forceinline__ void tile_update(double* __restrict__ C, int64_t ldc, int64_t cm0,
-                                            int64_t cn0, const double* __restrict__ A, int64_t lda,
-                                            int64_t am0, int64_t ak0, const double* __restrict__ B,
-                                            int64_t ldb, int64_t bk0, int64_t bn0) {
-  __shared__ double as[NB][NB + 1];   // [q][m]
-  __shared__ double bs[NB][NB + 1];   // [q][n]
+__device__ __forceinline__ void tile_update_lds(double* __restrict__ C, int64_t ldc, int64_t cm0,
+                                                int64_t cn0, const double* __restrict__ A,
+                                                int64_t lda, int64_t am0, int64_t ak0,
+                                                const double* __restrict__ B, int64_t ldb,
+                                                int64_t bk0, int64_t bn0, double* smem) {
+  typedef double Row[NB + 1];
+  Row* as = reinterpret_cast<Row*>(smem);                  // [q][m]
+  Row* bs = reinterpret_cast<Row*>(smem + NB * (NB + 1));  // [q][n]
   constexpr int PER = NB * NB / kThreads;
   const int tid = threadIdx.x;
   const int tx = tid & 15, ty = tid >> 4;
@@ -376,12 +386,13 @@ __device__ __forceinline__ void tile_update(double* __restrict__ C, int64_t ldc,
     }
 }
 
-__global__ __launch_bounds__(kThreads) void panel_solve(double* __restrict__ A, int64_t lda, int64_t k,
-                                                        const double* __restrict__ Dinv) {
-  const int64_t k0 = k * NB;
-  const int64_t r0 = k0 + NB + static_cast<int64_t>(blockIdx.x) * NB;
-  // out[i][c] = sum_q A[r0+i][k0+q] Dinv_k[c][q]
-  tile_update<false, true>(A, lda, r0, k0, A, lda, r0, k0, Dinv + k * NB * NB, NB, 0, 0);
+template <bool BNN, bool STORE = false>
+__device__ __forceinline__ void tile_update(double* __restrict__ C, int64_t ldc, int64_t cm0,
+                                            int64_t cn0, const double* __restrict__ A, int64_t lda,
+                                            int64_t am0, int64_t ak0, const double* __restrict__ B,
+                                            int64_t ldb, int64_t bk0, int64_t bn0) {
+  __shared__ double smem[2 * NB * (NB + 1)];
+  tile_update_lds<BNN, STORE>(C, ldc, cm0, cn0, A, lda, am0, ak0, B, ldb, bk0, bn0, smem);
 }
 
 // Cholesky trailing update after block column k: lower tiles (ti >= tj) of the
@@ -395,12 +406,33 @@ __global__ __launch_bounds__(kThreads) void chol_trailing(double* __restrict__ A
   tile_update<false>(A, lda, i0, j0, A, lda, i0, k0, A, lda, k0, j0);
 }
 
-// The same update restricted to block column k + 1 (the next diagonal block's column).
-__global__ __launch_bounds__(kThreads) void chol_trailing_col(double* __restrict__ A, int64_t lda,
-                                                              int64_t k) {
+// Rows below block k:  A[i][k-block] <- A[i][k-block] * Dinv_k^T.  One 64-row tile
+// per workgroup.
+__global__ __launch_bounds__(kThreads) void panel_solve(double* __restrict__ A, int64_t lda, int64_t k,
+                                                        const double* __restrict__ Dinv) {
+  const int64_t k0 = k * NB;
+  const int64_t r0 = k0 + NB + static_cast<int64_t>(blockIdx.x) * NB;
+  // out[i][c] = sum_q A[r0+i][k0+q] Dinv_k[c][q]
+  tile_update<false, true>(A, lda, r0, k0, A, lda, r0, k0, Dinv + k * NB * NB, NB, 0, 0);
+}
+
+// The update of block column k + 1 by panel k, A(i,k+1) -= L(i,k) L(k+1,k)^T for the block
+// rows i > k, and then, in workgroup 0 (whose tile is the next diagonal block), the
+// factorisation and inverse of diagonal block k + 1: one launch on the critical chain.
+constexpr int kStepLds = (kDiagLds > 2 * NB * (NB + 1)) ? kDiagLds : 2 * NB * (NB + 1);
+
+__global__ __launch_bounds__(kThreads) void col_diag(double* __restrict__ A, int64_t lda, int64_t k,
+                                                     const double* __restrict__ diag0,
+                                                     double* __restrict__ Dinv,
+                                                     uint32_t* __restrict__ flag) {
+  __shared__ double smem[kStepLds];
   const int64_t j0 = (k + 1) * NB;
   const int64_t i0 = j0 + static_cast<int64_t>(blockIdx.x) * NB, k0 = k * NB;
-  tile_update<false>(A, lda, i0, j0, A, lda, i0, k0, A, lda, k0, j0);
+  tile_update_lds<false>(A, lda, i0, j0, A, lda, i0, k0, A, lda, k0, j0, smem);
+  if (blockIdx.x == 0) {
+    __syncthreads();
+    factor_diag(A, lda, k + 1, diag0, Dinv, flag, smem);
+  }
 }
 
 // Inverse step i, part 1: X[i][j-block] = Dinv_i * S[i][j-block] for j <= i, in place.
@@ -453,7 +485,7 @@ size_t rfactor_ws_bytes(int64_t d) {
   size_t b = 0;
   b += align256(static_cast<size_t>(dp) * dp * sizeof(double));   // A -> L
   b += align256(static_cast<size_t>(dp) * dp * sizeof(double));   // S -> X = L^{-1}
-  b += align256(static_cast<size_t>(nblk) * NB * NB * sizeof(double));
+  b += align256(static_cast<size_t>(nblk) * NB * NB * sizeof(double));   // Dinv
   b += align256(static_cast<size_t>(dp) * sizeof(double));
   return b;
 }
@@ -492,13 +524,13 @@ Lookahead* lookahead() {
 // inverses of the diagonal blocks in Dinv and, when X is given, X = L^{-1}.
 //
 // Look-ahead schedule.  The caller's stream runs the critical chain: per block column
-// k the diagonal block, the panel below it, and the trailing update of block column
-// k + 1 only (all the next diagonal block needs).  A second stream applies block column
-// k to the rest of the trailing matrix (columns >= k + 2) while the chain moves on; a
-// third runs inverse step k (X row block k and its update of the rows below) as soon as
-// the panel of k is done.  The update of column k + 1 waits for the previous step's
-// rest update, so every tile still receives its updates in order of k, and the results
-// are those of the one-stream order.
+// k the panel below diagonal block k, then one launch (col_diag) that updates block
+// column k + 1 and factors diagonal block k + 1.  A second stream applies block column k
+// to the rest of the trailing matrix (columns >= k + 2) while the chain moves on; a third
+// runs inverse step k (X row block k and its update of the rows below) as soon as the
+// panel of k is done.  The update of column k + 1 waits for the previous step's rest
+// update, so every tile still receives its updates in order of k, and the results are
+// those of the one-stream order.
 int factor_reversed(const float* H, int64_t d, const int32_t* perm, double* A, int64_t dp,
                     double* Dinv, double* diag0, double* X, uint32_t* flag, hipStream_t s) {
   const int64_t nblk = dp / NB;
@@ -520,10 +552,10 @@ int factor_reversed(const float* H, int64_t d, const int32_t* perm, double* A, i
     fill_identity<<<grid_for(dp * dp), kThreads, 0, s>>>(X, dp);
     QZ_TRY(check_launch("rfactor.fill"));
   }
+  diag_block_panels<<<1, kDiagThreads, 0, s>>>(A, dp, 0, diag0, Dinv, flag);
+  QZ_TRY(check_launch("rfactor.diag"));
   for (int64_t k = 0; k < nblk; ++k) {
     const int64_t below = nblk - k - 1;
-    diag_block_panels<<<1, kDiagThreads, 0, s>>>(A, dp, k, diag0, Dinv, flag);
-    QZ_TRY(check_launch("rfactor.diag"));
     if (below > 0) {
       panel_solve<<<static_cast<unsigned>(below), kThreads, 0, s>>>(A, dp, k, Dinv);
       QZ_TRY(check_launch("rfactor.panel"));
@@ -533,8 +565,8 @@ int factor_reversed(const float* H, int64_t d, const int32_t* perm, double* A, i
     if (X) QZ_TRY(fork(s_inv, la ? la->ev_panel : nullptr));
     if (below > 0) {
       if (k > 0) QZ_TRY(fork(s, la ? la->ev_trail : nullptr));   // rest update of k - 1 done
-      chol_trailing_col<<<static_cast<unsigned>(below), kThreads, 0, s>>>(A, dp, k);
-      QZ_TRY(check_launch("rfactor.trailing_col"));
+      col_diag<<<static_cast<unsigned>(below), kThreads, 0, s>>>(A, dp, k, diag0, Dinv, flag);
+      QZ_TRY(check_launch("rfactor.coldiag"));
     }
     if (below > 1) {
       chol_trailing<<<static_cast<unsigned>((below - 1) * below / 2), kThreads, 0, s_trail>>>(
