@@ -26,8 +26,10 @@
  *   buffer gives QZ_EWORKSPACE.  Other arrays need only their element type's
  *   alignment (vector paths check and fall back to element access).
  *   Library-owned resources are per host thread and device and created on
- *   first use: two side streams for the GPTQ factorisation and a rocBLAS
- *   handle for the eigen-solver (which works in the caller's workspace).
+ *   first use: three streams for the GPTQ factorisation (two side streams and
+ *   one it records its HIP graph on), that graph (kept while the call's
+ *   arguments repeat), and a rocBLAS handle for the eigen-solver (which works
+ *   in the caller's workspace).
  * - Matrices are dense row-major with the leading dimension equal to the
  *   column count, unless an ld argument is given.
  * - Arguments are checked before anything is enqueued; on a non-OK return the
@@ -164,7 +166,11 @@ int qz_rtn_noalloc(const void* W, int32_t wt, int64_t d_o, int64_t d_i, const qz
  * inverse) and used in fp32; the factorisation runs part of its work on two
  * library-owned side streams (default priority, one pair per host thread and
  * device) that join `stream` before the call goes on, so the call still orders
- * on `stream` only.  SYNC: the codes and the grid are complete when the call
+ * on `stream` only.  The factorisation's operations are recorded once into a
+ * HIP graph and replayed with one launch on `stream` while H, perm, the
+ * workspace and the sizes are the same pointers and values as in the previous
+ * call on this host thread and device (the graph reads the buffers' current
+ * contents); a `stream` that is being captured gets the operations directly.  SYNC: the codes and the grid are complete when the call
  * returns; QZ_ENOTPD when a pivot of the factorisation is <= 1e-12 of its
  * diagonal entry (or not finite), QZ_ENONFINITE for non-finite H or W_hat.   */
 size_t qz_gptq_workspace(int64_t d_o, int64_t d_i, int32_t B);

@@ -605,8 +605,10 @@ __global__ void pivots_from_factor(const double* __restrict__ A, int64_t lda, in
 
 }  // namespace
 
-int rfactor(const float* H, int64_t d, const int32_t* perm, float* Rt, int64_t ldr, void* ws,
-            uint32_t* flag, hipStream_t s) {
+namespace {
+
+int rfactor_enqueue(const float* H, int64_t d, const int32_t* perm, float* Rt, int64_t ldr,
+                    void* ws, uint32_t* flag, hipStream_t s) {
   const int64_t dp = round_up(d, NB);
   const int64_t nblk = dp / NB;
   Carver cv(ws);
@@ -617,6 +619,74 @@ int rfactor(const float* H, int64_t d, const int32_t* perm, float* Rt, int64_t l
   QZ_TRY(factor_reversed(H, d, perm, A, dp, Dinv, diag0, X, flag, s));
   extract_rt<<<grid_for(d * d), kThreads, 0, s>>>(X, dp, d, Rt, ldr);
   return check_launch("rfactor.extract");
+}
+
+// The R factor enqueues about 11 operations per 64-column step (launches, event records
+// and cross-stream waits), which the host issues more slowly than the GPU runs them.  So
+// the whole sequence is captured once into a HIP graph (on a private capture stream, the
+// side streams joining through the same events) and replayed with one launch while the
+// arguments stay the same; one graph is kept per host thread and device, rebuilt when
+// any argument changes.  A caller's stream that is itself being captured gets the
+// operations directly.
+struct RGraph {
+  int device = -1;
+  hipStream_t cap = nullptr;
+  hipGraphExec_t exec = nullptr;
+  const float* H = nullptr;
+  int64_t d = -1;
+  const int32_t* perm = nullptr;
+  float* Rt = nullptr;
+  int64_t ldr = -1;
+  void* ws = nullptr;
+  uint32_t* flag = nullptr;
+};
+
+RGraph* rgraph() {
+  thread_local std::vector<RGraph> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  for (RGraph& g : cache)
+    if (g.device == dev) return g.cap ? &g : nullptr;
+  RGraph g;
+  g.device = dev;
+  if (hipStreamCreateWithFlags(&g.cap, hipStreamNonBlocking) != hipSuccess) g.cap = nullptr;
+  cache.push_back(g);
+  return cache.back().cap ? &cache.back() : nullptr;
+}
+
+}  // namespace
+
+int rfactor(const float* H, int64_t d, const int32_t* perm, float* Rt, int64_t ldr, void* ws,
+            uint32_t* flag, hipStream_t s) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &st) != hipSuccess) st = hipStreamCaptureStatusActive;
+  RGraph* g = (st == hipStreamCaptureStatusNone && lookahead()) ? rgraph() : nullptr;
+  if (!g) return rfactor_enqueue(H, d, perm, Rt, ldr, ws, flag, s);
+  const bool same = g->exec && g->H == H && g->d == d && g->perm == perm && g->Rt == Rt &&
+                    g->ldr == ldr && g->ws == ws && g->flag == flag;
+  if (!same) {
+    if (g->exec) {
+      QZ_HIP(hipGraphExecDestroy(g->exec));
+      g->exec = nullptr;
+    }
+    QZ_HIP(hipStreamBeginCapture(g->cap, hipStreamCaptureModeThreadLocal));
+    const int rc = rfactor_enqueue(H, d, perm, Rt, ldr, ws, flag, g->cap);
+    hipGraph_t graph = nullptr;
+    const hipError_t e = hipStreamEndCapture(g->cap, &graph);
+    if (rc != QZ_OK || e != hipSuccess) {
+      if (graph) (void)hipGraphDestroy(graph);
+      return rc != QZ_OK ? rc : fail(QZ_EHIP, "rfactor: graph capture failed");
+    }
+    const hipError_t ei = hipGraphInstantiate(&g->exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (ei != hipSuccess) {
+      g->exec = nullptr;
+      return fail(QZ_EHIP, "rfactor: graph instantiation failed");
+    }
+    g->H = H; g->d = d; g->perm = perm; g->Rt = Rt; g->ldr = ldr; g->ws = ws; g->flag = flag;
+  }
+  QZ_HIP(hipGraphLaunch(g->exec, s));
+  return QZ_OK;
 }
 
 int order_pivots(const float* H, int64_t d, const int32_t* perm, double* D, void* ws,

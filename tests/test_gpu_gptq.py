@@ -139,3 +139,46 @@ def test_gptq_deterministic_and_errors():
     with pytest.raises(q.QzError) as e:
         q.qz_gptq(Hd, Wd, 4, 128, 129)
     assert e.value.status == -1
+
+
+def test_gptq_rfactor_graph_replays_follow_their_inputs():
+    """The R factor is replayed from a captured graph while its arguments (pointers and
+    sizes) stay the same.  Replays with the same workspace must give the codes of a fresh
+    capture (a new workspace), also after the Hessian's values change in place and after
+    another shape has been factored in between, with host work and synchronisation
+    between the calls."""
+    import torch
+    q = qz()
+    H, W = _tiny()
+    Hd, Wd = to_dev(H.astype(np.float32)), to_dev(W)
+    n_ws = q.qz_gptq_workspace(W.shape[0], W.shape[1], 32)
+    ws = torch.empty(n_ws, dtype=torch.uint8, device="cuda")
+    X2 = qz_synth.calib_bf16(9, 1024, 256, p_out=0.02, f_out=30.0)
+    H2, _ = hessian.hessian(X2, 0.01)
+    W2 = qz_synth.weights_bf16(9, 48, 256)
+    H2d, W2d = to_dev(H2.astype(np.float32)), to_dev(W2)
+    ws2 = torch.empty(q.qz_gptq_workspace(48, 256, 64), dtype=torch.uint8, device="cuda")
+
+    def run(Hx, Wx, bits, group, B, w):
+        out = to_host(q.qz_gptq(Hx, Wx, bits, group, B, ws=w)[0])
+        torch.cuda.synchronize()
+        return out
+
+    first = run(Hd, Wd, 4, 128, 32, ws)
+    for _ in range(3):
+        _ = torch.randn(1000, device="cuda").sum().item()   # eager work in between
+        np.testing.assert_array_equal(run(Hd, Wd, 4, 128, 32, ws), first)
+    other = run(H2d, W2d, 3, 32, 64, ws2)
+    np.testing.assert_array_equal(run(Hd, Wd, 4, 128, 32, ws), first)
+    np.testing.assert_array_equal(run(H2d, W2d, 3, 32, 64, ws2), other)
+    # the Hessian changes in place: the replay reads the new values
+    Hd.mul_(1.0)
+    Hd[:, 3] *= 4.0
+    Hd[3, :] *= 4.0
+    replay = run(Hd, Wd, 4, 128, 32, ws)
+    fresh = run(Hd, Wd, 4, 128, 32, torch.empty(n_ws, dtype=torch.uint8, device="cuda"))
+    np.testing.assert_array_equal(replay, fresh)
+    H_new = to_host(Hd).astype(np.float64)
+    s, z = grid.fit_grid_f32(W, 4, 128)
+    ref, _ = gptq.gptq(H_new, W, s, z, 4, 128, hint=replay)
+    np.testing.assert_array_equal(replay, ref)
