@@ -26,10 +26,11 @@
  *   buffer gives QZ_EWORKSPACE.  Other arrays need only their element type's
  *   alignment (vector paths check and fall back to element access).
  *   Library-owned resources are per host thread and device and created on
- *   first use: three streams for the GPTQ factorisation (two side streams and
- *   one it records its HIP graph on), that graph (kept while the call's
- *   arguments repeat), and a rocBLAS handle for the eigen-solver (which works
- *   in the caller's workspace).
+ *   first use: four streams for GPTQ (two side streams of the factorisation,
+ *   one for the grid fit beside it, one the factorisation's HIP graph is
+ *   recorded on), that graph (kept while the call's arguments repeat), and a
+ *   rocBLAS handle for the eigen-solver (which works in the caller's
+ *   workspace).
  * - Matrices are dense row-major with the leading dimension equal to the
  *   column count, unless an ld argument is given.
  * - Arguments are checked before anything is enqueued; on a non-OK return the

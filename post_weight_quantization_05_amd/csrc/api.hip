@@ -228,6 +228,11 @@ size_t qz_gptq_workspace(int64_t d_o, int64_t d_i, int32_t B) {
   return gptq_ws(d_o, d_i);
 }
 
+static int gptq_blocks(float* Wf, int64_t ldw, float* E, int64_t lde, const float* Rt, int64_t ldr,
+                       int64_t d_o, int64_t d_i, const qz_grid* grid, int32_t B,
+                       const int32_t* perm, uint8_t* codes, int32_t* codes32, float* scales,
+                       uint8_t* zeros, int64_t G, int64_t SB, hipStream_t stream);
+
 // GPTQ with u8 codes clamped to the grid (codes) or unclamped int32 codes (codes32).
 static int gptq_run(const float* H, const void* W_hat, int32_t wt, int64_t d_o, int64_t d_i,
                     const qz_grid* grid, int32_t B, const int32_t* perm, uint8_t* codes,
@@ -270,23 +275,38 @@ static int gptq_run(const float* H, const void* W_hat, int32_t wt, int64_t d_o, 
     QZ_TRY(read_flag(flag, stream, &hp));
     if (hp & FLAG_BADARG) return fail(QZ_EINVAL, "gptq: perm is not a permutation of 0..d_i-1");
   }
+  // the grid and the fp32 copy of W need nothing from R: they run beside it
+  hipStream_t side = stream;
+  QZ_TRY(side_fork(stream, &side));
   if (d_o > 0) {
-    ScopedTimer tm(K_GRID_RTN, stream);
+    ScopedTimer tm(K_GRID_RTN, side);
     if (!(grid->flags & QZ_GRID_CALLER))
       QZ_TRY(launch_grid_fit(W_hat, wt, d_o, d_i, grid->group_size, grid->bits, scales, zeros,
-                             nullptr, nullptr, flag, stream));
-    QZ_TRY(launch_to_f32(W_hat, wt, d_o, d_i, perm, nullptr, Wf, ldw, flag, stream));
+                             nullptr, nullptr, flag, side));
+    QZ_TRY(launch_to_f32(W_hat, wt, d_o, d_i, perm, nullptr, Wf, ldw, flag, side));
   }
   {
     ScopedTimer tm(K_RFACTOR, stream);
     QZ_TRY(rfactor(H, d_i, perm, Rt, ldr, rws, flag, stream));
   }
+  QZ_TRY(side_join(stream, side));
+  // The factorisation's status is read once, at the end (the call's sync point): the
+  // block loop is enqueued while R is still being formed, and after a failed
+  // factorisation it only produces outputs that the error return leaves unspecified.
+  if (d_o > 0) QZ_TRY(gptq_blocks(Wf, ldw, E, lde, Rt, ldr, d_o, d_i, grid, B, perm, codes,
+                                  codes32, scales, zeros, G, SB, stream));
   uint32_t h = 0;
-  QZ_TRY(read_flag(flag, stream, &h));
+  QZ_TRY(read_flag(flag, stream, &h));   // SYNC: codes and grid are complete on return
   if (h & FLAG_NONFINITE) return fail(QZ_ENONFINITE, "gptq: non-finite H or W_hat");
   if (h & FLAG_NOTPD) return fail(QZ_ENOTPD, "gptq: H is not positive definite (increase damping)");
-  if (d_o == 0) return QZ_OK;
+  return QZ_OK;
+}
 
+// The block loop of GPTQ (after R): per block the in-block kernel, then the lazy updates.
+static int gptq_blocks(float* Wf, int64_t ldw, float* E, int64_t lde, const float* Rt, int64_t ldr,
+                       int64_t d_o, int64_t d_i, const qz_grid* grid, int32_t B,
+                       const int32_t* perm, uint8_t* codes, int32_t* codes32, float* scales,
+                       uint8_t* zeros, int64_t G, int64_t SB, hipStream_t stream) {
   auto update = [&](const float* Eop, int64_t K, int64_t col0, int64_t ncols, int64_t rk) {
     // W[:, col0 : col0 + ncols] -= Eop[:, 0:K] R[rk : rk + K, col0 : col0 + ncols]
     GemmArgs g{};
@@ -317,8 +337,6 @@ static int gptq_run(const float* H, const void* W_hat, int32_t wt, int64_t d_o, 
     }
     if (Aend < d_i) QZ_TRY(update(E, Aend - A, Aend, d_i - Aend, A));   // every later column
   }
-  // SYNC: the codes and the grid are complete when the call returns
-  QZ_HIP(hipStreamSynchronize(stream));
   return QZ_OK;
 }
 

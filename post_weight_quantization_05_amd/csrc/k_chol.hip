@@ -500,6 +500,8 @@ struct Lookahead {
   bool ok = false;
   hipStream_t trail = nullptr, inv = nullptr;
   hipEvent_t ev_panel = nullptr, ev_trail = nullptr, ev_join1 = nullptr, ev_join2 = nullptr;
+  hipStream_t side = nullptr;                        // work beside the factorisation
+  hipEvent_t ev_fork = nullptr, ev_back = nullptr;
 };
 
 Lookahead* lookahead() {
@@ -512,13 +514,43 @@ Lookahead* lookahead() {
   l.device = dev;
   l.ok = hipStreamCreateWithFlags(&l.trail, hipStreamNonBlocking) == hipSuccess &&
          hipStreamCreateWithFlags(&l.inv, hipStreamNonBlocking) == hipSuccess &&
+         hipStreamCreateWithFlags(&l.side, hipStreamNonBlocking) == hipSuccess &&
          hipEventCreateWithFlags(&l.ev_panel, hipEventDisableTiming) == hipSuccess &&
          hipEventCreateWithFlags(&l.ev_trail, hipEventDisableTiming) == hipSuccess &&
          hipEventCreateWithFlags(&l.ev_join1, hipEventDisableTiming) == hipSuccess &&
-         hipEventCreateWithFlags(&l.ev_join2, hipEventDisableTiming) == hipSuccess;
+         hipEventCreateWithFlags(&l.ev_join2, hipEventDisableTiming) == hipSuccess &&
+         hipEventCreateWithFlags(&l.ev_fork, hipEventDisableTiming) == hipSuccess &&
+         hipEventCreateWithFlags(&l.ev_back, hipEventDisableTiming) == hipSuccess;
   cache.push_back(l);
   return cache.back().ok ? &cache.back() : nullptr;
 }
+
+}  // namespace
+
+// A stream for work that may run beside the factorisation: `s` itself when the library's
+// streams are unavailable; otherwise a stream of its own (not one the factorisation
+// uses), made to wait for everything enqueued on `s` so far.  side_join makes `s` wait
+// for what was enqueued there since.
+int side_fork(hipStream_t s, hipStream_t* side) {
+  Lookahead* la = lookahead();
+  *side = s;
+  if (!la) return QZ_OK;
+  QZ_HIP(hipEventRecord(la->ev_fork, s));
+  QZ_HIP(hipStreamWaitEvent(la->side, la->ev_fork, 0));
+  *side = la->side;
+  return QZ_OK;
+}
+
+int side_join(hipStream_t s, hipStream_t side) {
+  if (side == s) return QZ_OK;
+  Lookahead* la = lookahead();
+  if (!la) return QZ_OK;
+  QZ_HIP(hipEventRecord(la->ev_back, side));
+  QZ_HIP(hipStreamWaitEvent(s, la->ev_back, 0));
+  return QZ_OK;
+}
+
+namespace {
 
 // The reversed-order Cholesky in place, A (lower) = L with L L^T = J Hp J, plus the
 // inverses of the diagonal blocks in Dinv and, when X is given, X = L^{-1}.

@@ -214,6 +214,10 @@ int rfactor(const float* H, int64_t d, const int32_t* perm, float* Rt, int64_t l
 // first, i.e. 1 / R_jj^2 of GPTQ's factor.  Same workspace and flags as rfactor.
 int order_pivots(const float* H, int64_t d, const int32_t* perm, double* D, void* ws,
                  uint32_t* flag, hipStream_t s);
+// A stream for work beside the factorisation (waits for what `s` holds so far; `s`
+// itself without side streams), and the join back into `s`.
+int side_fork(hipStream_t s, hipStream_t* side);
+int side_join(hipStream_t s, hipStream_t side);
 
 // GPTQ in-block column kernel (k_gptq.hip)
 int launch_gptq_block(float* W, int64_t ldw, int64_t d_o, int64_t a, int64_t b, const float* Rt,
