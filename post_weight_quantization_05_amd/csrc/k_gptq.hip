@@ -10,8 +10,8 @@
 // through the columns for all of them together.  The 16 lanes of a DPP row share one
 // weight row; lane l keeps columns l, l+16, ..., l+112 of the block in registers, with
 // its row's (scale, zero) for each of them, so neither the block of W nor the grid
-// passes through LDS.  At step j the lane holding column j rounds it (IEEE fp32
-// division, half-to-even) and forms the scaled error, a DPP row broadcast
+// passes through LDS.  At step j the lane holding column j rounds it (the correctly
+// rounded fp32 quotient, half-to-even) and forms the scaled error, a DPP row broadcast
 // (row_newbcast) hands it to the other fifteen lanes, and each lane updates its later
 // columns with its eight entries of R's row j, read from LDS as two 16-byte vectors.
 // The workgroup's set-up stages R's block with many global loads in flight (clamped
@@ -35,10 +35,25 @@ __device__ __forceinline__ float row_bcast(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + O, 0xF, 0xF, false));
 }
 
-// Unclamped code rint(x / s) + z, kept inside the int32 range.
-__device__ __forceinline__ float quant_code_noclip(float x, float s, float z) {
-  const float u = __builtin_rintf(x / s) + z;
-  return fminf(fmaxf(u, -2147483648.0f), 2147483520.0f);
+// The correctly rounded quotient x / s from y = RN(1 / s), formed once per column: with
+// q0 = RN(x y) within an ulp of x / s, the remainder x - s q0 is exact in one FMA and
+// RN(q0 + r y) is RN(x / s) (Markstein's theorem on division by a correctly rounded
+// reciprocal), so the codes are those of the IEEE division at three operations instead of
+// the eleven of the full division sequence on the step's dependency chain.  (Values whose
+// quotient or remainder leaves the normal range only reach codes that the rounding and
+// the clamp make the same.)
+__device__ __forceinline__ float div_rn(float x, float s, float y) {
+  const float q0 = x * y;
+  const float r = __builtin_fmaf(-s, q0, x);
+  return __builtin_fmaf(r, y, q0);
+}
+
+// Clamped and unclamped (kept inside the int32 range) codes rint(x / s) + z.
+__device__ __forceinline__ float code_of(float q, float z, float maxq) {
+  return fminf(fmaxf(__builtin_rintf(q) + z, 0.0f), maxq);
+}
+__device__ __forceinline__ float code_of_noclip(float q, float z) {
+  return fminf(fmaxf(__builtin_rintf(q) + z, -2147483648.0f), 2147483520.0f);
 }
 
 // Entries l + 16 i of R's row j and 1 / R_jj, read from LDS one step ahead.
@@ -56,12 +71,13 @@ __device__ __forceinline__ void load_rrow(RRow& r, const float* Rb, const float*
 
 template <int J, bool NOCLIP>
 __device__ __forceinline__ void column_step(float (&wr)[PER], float (&cr)[PER], const float (&sv)[PER],
-                                            const float (&zv)[PER], float maxq, const RRow& r,
-                                            int l) {
+                                            const float (&yv)[PER], const float (&zv)[PER],
+                                            float maxq, const RRow& r, int l) {
   constexpr int owner = J % LPR, slot = J / LPR;
   // every lane rounds its own value of slot `slot`; only the owner's is used
   const float x = wr[slot];
-  const float c = NOCLIP ? quant_code_noclip(x, sv[slot], zv[slot]) : quant_code(x, sv[slot], zv[slot], maxq);
+  const float q = div_rn(x, sv[slot], yv[slot]);
+  const float c = NOCLIP ? code_of_noclip(q, zv[slot]) : code_of(q, zv[slot], maxq);
   const float qv = sv[slot] * (c - zv[slot]);
   const float err = (x - qv) * r.rinv;
   const bool own = (l == owner);
@@ -79,23 +95,23 @@ __device__ __forceinline__ void column_step(float (&wr)[PER], float (&cr)[PER], 
 template <int J, bool NOCLIP>
 struct Steps {
   __device__ static __forceinline__ void run(int w, float (&wr)[PER], float (&cr)[PER],
-                                             const float (&sv)[PER], const float (&zv)[PER],
-                                             float maxq, const float* Rb, const float* rinv,
-                                             const RRow& cur, int l) {
+                                             const float (&sv)[PER], const float (&yv)[PER],
+                                             const float (&zv)[PER], float maxq, const float* Rb,
+                                             const float* rinv, const RRow& cur, int l) {
     if (J >= w) return;   // uniform: blocks narrower than MAXB stop early
     RRow next;
     if (J + 1 < MAXB) load_rrow(next, Rb, rinv, J + 1 < MAXB ? J + 1 : J, l);
-    column_step<J, NOCLIP>(wr, cr, sv, zv, maxq, cur, l);
+    column_step<J, NOCLIP>(wr, cr, sv, yv, zv, maxq, cur, l);
     // one step's work per scheduling region: the next row's reads issue before it
     __builtin_amdgcn_sched_barrier(0);
-    Steps<J + 1, NOCLIP>::run(w, wr, cr, sv, zv, maxq, Rb, rinv, next, l);
+    Steps<J + 1, NOCLIP>::run(w, wr, cr, sv, yv, zv, maxq, Rb, rinv, next, l);
   }
 };
 template <bool NOCLIP>
 struct Steps<MAXB, NOCLIP> {
   __device__ static __forceinline__ void run(int, float (&)[PER], float (&)[PER], const float (&)[PER],
-                                             const float (&)[PER], float, const float*,
-                                             const float*, const RRow&, int) {}
+                                             const float (&)[PER], const float (&)[PER], float,
+                                             const float*, const float*, const RRow&, int) {}
 };
 
 // NOCLIP: codes are not clamped to [0, 2^b - 1] (the Babai page's no-clipping regime)
@@ -149,7 +165,7 @@ __global__ __launch_bounds__(ROWS * LPR) void gptq_block_kernel(
 
   // the row's block of W and, per owned column, the row's grid (groups are ranges of
   // ORIGINAL columns)
-  float wr[PER], sv[PER], zv[PER], cr[PER];
+  float wr[PER], sv[PER], yv[PER], zv[PER], cr[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int c = l + LPR * i;
@@ -157,6 +173,7 @@ __global__ __launch_bounds__(ROWS * LPR) void gptq_block_kernel(
     const int64_t oc = perm ? perm[a + cc] : a + cc;
     const int64_t gi = crow * G + oc / group;
     sv[i] = scales[gi];
+    yv[i] = 1.0f / sv[i];   // IEEE division: the correctly rounded reciprocal
     zv[i] = static_cast<float>(zeros[gi]);
     wr[i] = (rok && c < w) ? W[row * ldw + a + c] : 0.f;
     cr[i] = 0.f;
@@ -165,7 +182,7 @@ __global__ __launch_bounds__(ROWS * LPR) void gptq_block_kernel(
 
   RRow first;
   load_rrow(first, Rb, rinv, 0, l);
-  Steps<0, NOCLIP>::run(w, wr, cr, sv, zv, maxq, Rb, rinv, first, l);
+  Steps<0, NOCLIP>::run(w, wr, cr, sv, yv, zv, maxq, Rb, rinv, first, l);
 
   // E (the scaled errors, for the matrix-core update of the later columns) and the codes;
   // for each slot the 16 lanes of a row write 16 consecutive columns
