@@ -4,10 +4,12 @@ the 4096 x 4096 attention projection (W3), the 4096 -> 12288 up projection (W3, 
 headline layer, and W2 with 150 ADMM-Q iterations) and the 32B-like 5120 -> 25600 up
 projection (W3, 200 iterations, grid refresh every 10).
 
-H is built by the oracle from the first 16384 calibration tokens (the fp64 sum over all
-262144 tokens would take minutes on the host); the GPU's own full-token Hessian is
-checked separately (test_gpu_hessian.py::test_hessian_full_size_sampled).  ADMM-Q runs
-its whole trajectory on both sides."""
+H is built by the oracle from the first 16384 calibration tokens for the parametrised
+layers; the headline layer is also run with the H the benchmark itself uses, the fp64 sum
+over all 262144 tokens of its seeded draw (about 8 s of host BLAS).  The GPU's own
+full-token Hessian is checked entry by entry separately
+(test_gpu_hessian.py::test_hessian_full_size_every_entry).  ADMM-Q runs its whole
+trajectory on both sides."""
 import numpy as np
 import pytest
 
@@ -52,3 +54,42 @@ def test_admm_full_size_sampled_rows(name):
     cfg = L["cfg"]
     admm_rows_trajectory(name, L["Hf"], L["W"], sample_rows(cfg["d_o"]), cfg["bits"], cfg["group"],
                          cfg["iters"], cfg["rho0"], cfg["gamma"], cfg["refresh"], B=cfg["B"])
+
+
+def _headline_full_tokens():
+    """The headline layer with the benchmark's own input: H from all 262144 calibration
+    tokens (the bench's seeded draw), summed in fp64 by the oracle over token slices."""
+    key = "headline_full_tokens"
+    if key not in _cache:
+        _cache.clear()
+        import torch
+        from oracle import hessian
+        name = "up_4096x12288_w3g128"
+        cfg = qz_synth.WORKLOADS[name]
+        X = qz_synth.calib_bf16_torch(cfg["seed"], cfg["n"], cfg["d_i"], cfg["p_out"], cfg["f_out"])
+        G = np.zeros((cfg["d_i"], cfg["d_i"]))
+        for a in range(0, cfg["n"], 16384):
+            G += hessian.gram(to_host(X[a:a + 16384]), chunk=16384)
+        del X
+        torch.cuda.empty_cache()
+        H64 = G + hessian.damping(G, cfg["damp"]) * np.eye(cfg["d_i"])
+        W = qz_synth.weights_bf16(cfg["seed"], cfg["d_o"], cfg["d_i"])
+        _cache[key] = dict(name=name, cfg=cfg, Hf=H64.astype(np.float32), W=W)
+    return _cache[key]
+
+
+def test_gptq_headline_full_tokens_sampled_rows():
+    """GPTQ on the headline layer with the H the benchmark uses (all 262144 tokens)."""
+    L = _headline_full_tokens()
+    cfg = L["cfg"]
+    gptq_rows(L["name"] + "_262144tok", L["Hf"], L["W"], sample_rows(cfg["d_o"]), cfg["bits"],
+              cfg["group"], cfg["B"])
+
+
+def test_admm_headline_full_tokens_sampled_rows():
+    """ADMM-Q's whole trajectory on the headline layer with the H the benchmark uses."""
+    L = _headline_full_tokens()
+    cfg = L["cfg"]
+    admm_rows_trajectory(L["name"] + "_262144tok", L["Hf"], L["W"], sample_rows(cfg["d_o"]),
+                         cfg["bits"], cfg["group"], cfg["iters"], cfg["rho0"], cfg["gamma"],
+                         cfg["refresh"], B=cfg["B"])
