@@ -319,13 +319,19 @@ __device__ __forceinline__ void tri_tile(int64_t t, int64_t& ti, int64_t& tj) {
   tj = t - i * (i + 1) / 2;
 }
 
-// C[64x64 tile] -= A_op * B_op (STORE: C = A_op * B_op) with K = 64.
+// C[64x64 tile] -= A_op * B_op (STORE: C = A_op * B_op) with K = 64, on the fp64 matrix
+// cores.
 //  A_op[m][q] = A[(am0 + m) * lda + ak0 + q]
 //  B_op[q][n] = BNN ? B[(bk0 + q) * ldb + bn0 + n] : B[(bn0 + n) * ldb + bk0 + q]
 // Both operands are staged in LDS before any output is written, so C may alias them.
 // Every thread issues all of its operand loads (and, when updating, its 16 loads of C)
-// before waiting for any of them.  Threads own 4 x 4 outputs (rows ty + 16a, cols
-// tx + 16b).
+// before waiting for any of them.  Wavefront w computes the 32 x 32 quadrant at rows
+// 32 (w / 2), columns 32 (w % 2) as 2 x 2 blocks of v_mfma_f64_16x16x4 (16 x 4 times
+// 4 x 16 per instruction, 16 instructions along K).  Fragment layout of that instruction
+// (lane l): A[l % 16][l / 16], B[l / 16][l % 16], and result element i at D[l / 16 + 4 i]
+// [l % 16].  The products are summed from zero and subtracted from C once at the end.
+typedef double v4f64 __attribute__((ext_vector_type(4)));
+
 template <bool BNN, bool STORE = false>
 __device__ __forceinline__ void tile_update_lds(double* __restrict__ C, int64_t ldc, int64_t cm0,
                                                 int64_t cn0, const double* __restrict__ A,
@@ -337,8 +343,10 @@ __device__ __forceinline__ void tile_update_lds(double* __restrict__ C, int64_t 
   Row* bs = reinterpret_cast<Row*>(smem + NB * (NB + 1));  // [q][n]
   constexpr int PER = NB * NB / kThreads;
   const int tid = threadIdx.x;
-  const int tx = tid & 15, ty = tid >> 4;
-  double va[PER], vb[PER], cv[4][4];
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lr = lane >> 4, lc = lane & 15;
+  const int r0 = (wave >> 1) * 32, c0 = (wave & 1) * 32;
+  double va[PER], vb[PER], cv[2][2][4];
 #pragma unroll
   for (int t = 0; t < PER; ++t) {
     const int e = tid + t * kThreads;
@@ -348,9 +356,12 @@ __device__ __forceinline__ void tile_update_lds(double* __restrict__ C, int64_t 
   }
   if (!STORE) {
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) cv[a][b] = C[(cm0 + ty + 16 * a) * ldc + cn0 + tx + 16 * b];
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          cv[a][b][i] = C[(cm0 + r0 + 16 * a + lr + 4 * i) * ldc + cn0 + c0 + 16 * b + lc];
   }
 #pragma unroll
   for (int t = 0; t < PER; ++t) {
@@ -361,29 +372,29 @@ __device__ __forceinline__ void tile_update_lds(double* __restrict__ C, int64_t 
     else bs[c][r] = vb[t];
   }
   __syncthreads();
-  double acc[4][4];
+  v4f64 acc[2][2];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
-  for (int q = 0; q < NB; ++q) {
-    double av[4], bv[4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a) av[a] = as[q][ty + 16 * a];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) bv[b] = bs[q][tx + 16 * b];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) acc[a][b] = fma(av[a], bv[b], acc[a][b]);
+    for (int b = 0; b < 2; ++b) acc[a][b] = v4f64{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+  for (int q = 0; q < NB; q += 4) {
+    const double a0 = as[q + lr][r0 + lc], a1 = as[q + lr][r0 + 16 + lc];
+    const double b0 = bs[q + lr][c0 + lc], b1 = bs[q + lr][c0 + 16 + lc];
+    acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc[0][0], 0, 0, 0);
+    acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc[0][1], 0, 0, 0);
+    acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc[1][0], 0, 0, 0);
+    acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc[1][1], 0, 0, 0);
   }
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      double* c = C + (cm0 + ty + 16 * a) * ldc + cn0 + tx + 16 * b;
-      *c = STORE ? acc[a][b] : cv[a][b] - acc[a][b];
-    }
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        double* c = C + (cm0 + r0 + 16 * a + lr + 4 * i) * ldc + cn0 + c0 + 16 * b + lc;
+        *c = STORE ? acc[a][b][i] : cv[a][b][i] - acc[a][b][i];
+      }
 }
 
 template <bool BNN, bool STORE = false>
