@@ -73,49 +73,23 @@ __device__ __forceinline__ double rsqrt_f64(double p) {
 
 // Factor diagonal block k in place (lower) and write its inverse to Dinv[k]: four
 // wavefronts, the block held in LDS and factored right-looking over four 16-column panels:
-//   (1) wavefront 0 factors the panel's 16 x 16 diagonal sub-block: the four lanes of a
-//       quad share a sub-block row, lane q keeping columns q, q+4, q+8, q+12; per pivot j
-//       the pivot comes from its lane by readlane, the row's own column-j entry by a DPP
-//       quad broadcast, and the column entries L[l][j] the lane needs by ds_bpermute from
-//       the lanes of row l (no LDS round trip on the pivot chain);
-//   (2) wavefront 0 then solves the rows below against it, one lane per row holding the
-//       row's 16 entries (L[i][c] = (A[i][c] - sum_{m<c} L[i][m] L[c][m]) / L[c][c]);
-//   (3) all four wavefronts update the trailing lower triangle, A[i][j] -= sum over the
-//       panel of L[i][m] L[j][m], in 2 x 2 blocks; one barrier before (3), one after.
+//   (1) wavefront 0 factors the panel's rows c0 .. 63, one lane per row holding the row's
+//       16 panel entries in registers: per pivot j the pivot comes from lane j by readlane,
+//       each lane scales its own entry (L[i][j]) and updates its later entries with the
+//       column values L[c][j] read from lanes c by readlane.  The rows below the 16 x 16
+//       diagonal sub-block are solved by the same instructions;
+//   (2) all four wavefronts update the trailing lower triangle, A[i][j] -= sum over the
+//       panel of L[i][m] L[j][m], in 16 x 16 blocks on the matrix cores; one barrier
+//       before (2), one after.
 // The inverse: each wavefront inverts one 16 x 16 diagonal block of L by forward
 // substitution (one lane per column), then block forward substitution fills the blocks
 // below the diagonal.  Entries above the diagonal are never read as pivots or L entries
 // and are not stored.
+typedef double v4f64 __attribute__((ext_vector_type(4)));
+
 constexpr int PB = 16;                  // panel width
 constexpr int kDiagThreads = 256;
 constexpr int LS = NB + 1;              // LDS row stride of the block (doubles)
-
-template <int Q>
-__device__ __forceinline__ double quad_bcast(double v) {
-  constexpr int ctrl = Q | (Q << 2) | (Q << 4) | (Q << 6);   // quad_perm [Q, Q, Q, Q]
-  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), ctrl, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), ctrl, 0xF, 0xF, false);
-  return __hiloint2double(hi, lo);
-}
-__device__ __forceinline__ double quad_bcast_n(double v, int q) {
-  switch (q) {
-    case 0: return quad_bcast<0>(v);
-    case 1: return quad_bcast<1>(v);
-    case 2: return quad_bcast<2>(v);
-    default: return quad_bcast<3>(v);
-  }
-}
-// v of lane `src` (ds_bpermute: a crossbar read, no LDS memory)
-__device__ __forceinline__ double lane_read(double v, int src) {
-  const int lo = __builtin_amdgcn_ds_bpermute(src * 4, __double2loint(v));
-  const int hi = __builtin_amdgcn_ds_bpermute(src * 4, __double2hiint(v));
-  return __hiloint2double(hi, lo);
-}
-__device__ __forceinline__ void wave_sync_lds() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // LDS of factor_diag, in doubles: the block (then L), X = L^{-1}, 1 / L[r][r], the pivot
 // tolerances and three 16 x 16 staging blocks of the block substitution.
@@ -158,76 +132,49 @@ __device__ __forceinline__ void factor_diag(double* __restrict__ A, int64_t lda,
   bool notpd = false;
 #pragma unroll 1
   for (int c0 = 0; c0 < NB; c0 += PB) {
-    const int nrows = NB - c0 - PB;
     if (wave == 0) {
-      // (1) the 16 x 16 diagonal sub-block
-      double a[4];
+      // (1) the panel's rows c0 .. 63, one lane per row, 16 entries in registers
+      const bool act = lane < NB - c0;
+      const int i = c0 + (act ? lane : 0);
+      double v[PB];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) a[u] = S[(c0 + r) * LS + c0 + q + 4 * u];
-      const double tolr = tolv[c0 + r];
+      for (int m = 0; m < PB; ++m) v[m] = act ? S[i * LS + c0 + m] : 0.0;
+      const double tol = act ? tolv[i] : 0.0;
 #pragma unroll
       for (int j = 0; j < PB; ++j) {
-        const int ju = j >> 2, jq = j & 3;
-        const double p = readlane_f64(a[ju], 4 * j + jq);   // pivot, uniform
-        notpd = notpd || ((r == j) && (!(p > tolr) || !__builtin_isfinite(p)));
+        const double p = readlane_f64(v[j], j);               // pivot, uniform
+        notpd = notpd || (lane == j && (!(p > tol) || !__builtin_isfinite(p)));
         const double rj = rsqrt_f64(p > 0.0 ? p : 0.0);
-        const double own = quad_bcast_n(a[ju], jq);           // A[r][j] of this row
-        const double lrj = (r >= j) ? own * rj : 0.0;         // L[r][j]
+        const double t = (act && lane >= j) ? v[j] * rj : 0.0;   // L[i][c0 + j]
+        v[j] = t;
         if (lane == 0) rinv[c0 + j] = rj;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int l = q + 4 * u;
-          const double lc = lane_read(lrj, 4 * l);   // L[l][j] (zero for l < j)
-          a[u] = (l == j) ? lrj : fma(-lrj, lc, a[u]);
-        }
+        for (int c = j + 1; c < PB; ++c) v[c] = fma(-t, readlane_f64(t, c), v[c]);
       }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int c = q + 4 * u;
-        S[(c0 + r) * LS + c0 + c] = (c <= r) ? a[u] : 0.0;
-      }
-      wave_sync_lds();
-      // (2) the rows below, one lane per row
-      if (lane < nrows) {
-        const int i = c0 + PB + lane;
-        double v[PB];
-#pragma unroll
-        for (int m = 0; m < PB; ++m) v[m] = S[i * LS + c0 + m];
-#pragma unroll
-        for (int c = 0; c < PB; ++c) {
-          double acc = v[c];
-#pragma unroll
-          for (int m = 0; m < c; ++m) acc = fma(-v[m], S[(c0 + c) * LS + c0 + m], acc);
-          v[c] = acc * rinv[c0 + c];
-        }
+      if (act) {
 #pragma unroll
         for (int m = 0; m < PB; ++m) S[i * LS + c0 + m] = v[m];
       }
     }
     __syncthreads();
-    // (3) trailing lower triangle, 2 x 2 blocks
-    if (nrows > 0) {
-      const int nb = nrows / 2;
-      const int base = c0 + PB;
-      for (int t = tid; t < nb * nb; t += kDiagThreads) {
-        const int bi = t / nb, bj = t % nb;
-        if (bj > bi) continue;
-        const int i0 = base + 2 * bi, j0 = base + 2 * bj;
-        double s00 = 0.0, s01 = 0.0, s10 = 0.0, s11 = 0.0;
+    // (2) trailing lower triangle, rows and columns c0 + 16 .. 63, in 16 x 16 blocks on the
+    // matrix cores (K = 16: four v_mfma_f64_16x16x4)
+    const int nbt = (NB - c0 - PB) / 16;
+    const int lr = lane >> 4, lc = lane & 15;
+    for (int t = wave; t < nbt * (nbt + 1) / 2; t += kDiagThreads / 64) {
+      int bi = 0;
+      while ((bi + 1) * (bi + 2) / 2 <= t) ++bi;
+      const int bj = t - bi * (bi + 1) / 2;
+      const int rb = c0 + PB + 16 * bi, cb = c0 + PB + 16 * bj;
+      v4f64 acc = v4f64{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-        for (int m = 0; m < PB; ++m) {
-          const double li0 = S[i0 * LS + c0 + m], li1 = S[(i0 + 1) * LS + c0 + m];
-          const double lj0 = S[j0 * LS + c0 + m], lj1 = S[(j0 + 1) * LS + c0 + m];
-          s00 = fma(li0, lj0, s00);
-          s01 = fma(li0, lj1, s01);
-          s10 = fma(li1, lj0, s10);
-          s11 = fma(li1, lj1, s11);
-        }
-        S[i0 * LS + j0] -= s00;
-        S[i0 * LS + j0 + 1] -= s01;
-        S[(i0 + 1) * LS + j0] -= s10;
-        S[(i0 + 1) * LS + j0 + 1] -= s11;
+      for (int k0 = 0; k0 < PB; k0 += 4) {
+        const double a = S[(rb + lc) * LS + c0 + k0 + lr];
+        const double bb = S[(cb + lc) * LS + c0 + k0 + lr];
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a, bb, acc, 0, 0, 0);
       }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) S[(rb + lr + 4 * q) * LS + cb + lc] -= acc[q];
     }
     __syncthreads();
   }
@@ -330,8 +277,6 @@ __device__ __forceinline__ void tri_tile(int64_t t, int64_t& ti, int64_t& tj) {
 // 4 x 16 per instruction, 16 instructions along K).  Fragment layout of that instruction
 // (lane l): A[l % 16][l / 16], B[l / 16][l % 16], and result element i at D[l / 16 + 4 i]
 // [l % 16].  The products are summed from zero and subtracted from C once at the end.
-typedef double v4f64 __attribute__((ext_vector_type(4)));
-
 template <bool BNN, bool STORE = false>
 __device__ __forceinline__ void tile_update_lds(double* __restrict__ C, int64_t ldc, int64_t cm0,
                                                 int64_t cn0, const double* __restrict__ A,
