@@ -95,10 +95,36 @@ constexpr int LS = NB + 1;              // LDS row stride of the block (doubles)
 // tolerances and three 16 x 16 staging blocks of the block substitution.
 constexpr int kDiagLds = 2 * NB * LS + 2 * NB + 3 * PB * (PB + 1);
 
-__device__ __forceinline__ void factor_diag(double* __restrict__ A, int64_t lda, int64_t k,
-                                            const double* __restrict__ diag0,
-                                            double* __restrict__ Dinv, uint32_t* __restrict__ flag,
-                                            double* smem) {
+// Diagonal block k of A into S (the LDS block of factor_diag, lower part, zero above the
+// diagonal) and the pivot tolerances into tolv.  All 16 loads of a thread are in flight at
+// once (every address lies inside A).
+__device__ __forceinline__ void diag_load(const double* __restrict__ A, int64_t lda, int64_t k,
+                                          const double* __restrict__ diag0, double* smem) {
+  double* S = smem;
+  double* tolv = smem + 2 * NB * LS + NB;
+  const int tid = threadIdx.x;
+  const int64_t k0 = k * NB;
+  constexpr int PER = NB * NB / kDiagThreads;
+  double v[PER];
+#pragma unroll
+  for (int t = 0; t < PER; ++t) {
+    const int e = tid + t * kDiagThreads;
+    v[t] = A[(k0 + e / NB) * lda + k0 + e % NB];
+  }
+  if (tid < NB) tolv[tid] = 1e-12 * diag0[k0 + tid];
+#pragma unroll
+  for (int t = 0; t < PER; ++t) {
+    const int e = tid + t * kDiagThreads;
+    const int i = e / NB, c = e % NB;
+    S[i * LS + c] = (c <= i) ? v[t] : 0.0;
+  }
+}
+
+// Factor the block held in S (and tolv) as above, write L to diagonal block k of A and
+// L^{-1} to Dinv[k].  The caller has filled S and tolv and passed a barrier.
+__device__ __forceinline__ void diag_factor_lds(double* __restrict__ A, int64_t lda, int64_t k,
+                                                double* __restrict__ Dinv,
+                                                uint32_t* __restrict__ flag, double* smem) {
   double* S = smem;                           // the block, then L (lower)
   double* Xf = S + NB * LS;                   // X = L^{-1}
   double* rinv = Xf + NB * LS;                // 1 / L[r][r]
@@ -106,28 +132,7 @@ __device__ __forceinline__ void factor_diag(double* __restrict__ A, int64_t lda,
   double* Tb = tolv + NB;                     // [3][PB][PB + 1]
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int r = lane >> 2, q = lane & 3;
   const int64_t k0 = k * NB;
-
-  // all 16 loads of a thread in flight at once (every address lies inside A; entries above
-  // the diagonal are replaced by zero afterwards)
-  {
-    constexpr int PER = NB * NB / kDiagThreads;
-    double v[PER];
-#pragma unroll
-    for (int t = 0; t < PER; ++t) {
-      const int e = tid + t * kDiagThreads;
-      v[t] = A[(k0 + e / NB) * lda + k0 + e % NB];
-    }
-    if (tid < NB) tolv[tid] = 1e-12 * diag0[k0 + tid];
-#pragma unroll
-    for (int t = 0; t < PER; ++t) {
-      const int e = tid + t * kDiagThreads;
-      const int i = e / NB, c = e % NB;
-      S[i * LS + c] = (c <= i) ? v[t] : 0.0;
-    }
-  }
-  __syncthreads();
 
   bool notpd = false;
 #pragma unroll 1
@@ -247,6 +252,15 @@ __device__ __forceinline__ void factor_diag(double* __restrict__ A, int64_t lda,
   }
 }
 
+__device__ __forceinline__ void factor_diag(double* __restrict__ A, int64_t lda, int64_t k,
+                                            const double* __restrict__ diag0,
+                                            double* __restrict__ Dinv, uint32_t* __restrict__ flag,
+                                            double* smem) {
+  diag_load(A, lda, k, diag0, smem);
+  __syncthreads();
+  diag_factor_lds(A, lda, k, Dinv, flag, smem);
+}
+
 __global__ __launch_bounds__(kDiagThreads) void diag_block_panels(double* __restrict__ A, int64_t lda,
                                                                   int64_t k,
                                                                   const double* __restrict__ diag0,
@@ -277,7 +291,7 @@ __device__ __forceinline__ void tri_tile(int64_t t, int64_t& ti, int64_t& tj) {
 // 4 x 16 per instruction, 16 instructions along K).  Fragment layout of that instruction
 // (lane l): A[l % 16][l / 16], B[l / 16][l % 16], and result element i at D[l / 16 + 4 i]
 // [l % 16].  The products are summed from zero and subtracted from C once at the end.
-template <bool BNN, bool STORE = false>
+template <bool BNN, bool STORE = false, bool TO_S = false>
 __device__ __forceinline__ void tile_update_lds(double* __restrict__ C, int64_t ldc, int64_t cm0,
                                                 int64_t cn0, const double* __restrict__ A,
                                                 int64_t lda, int64_t am0, int64_t ak0,
@@ -330,6 +344,21 @@ __device__ __forceinline__ void tile_update_lds(double* __restrict__ C, int64_t 
     acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc[0][1], 0, 0, 0);
     acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc[1][0], 0, 0, 0);
     acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc[1][1], 0, 0, 0);
+  }
+  if (TO_S) {
+    // the updated tile goes to the LDS block of the diagonal factorisation instead (lower
+    // part, zero above the diagonal), over the staging area once every wavefront is done
+    __syncthreads();
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = r0 + 16 * a + lr + 4 * i, n = c0 + 16 * b + lc;
+          smem[m * LS + n] = (n <= m) ? cv[a][b][i] - acc[a][b][i] : 0.0;
+        }
+    return;
   }
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -384,10 +413,14 @@ __global__ __launch_bounds__(kThreads) void col_diag(double* __restrict__ A, int
   __shared__ double smem[kStepLds];
   const int64_t j0 = (k + 1) * NB;
   const int64_t i0 = j0 + static_cast<int64_t>(blockIdx.x) * NB, k0 = k * NB;
-  tile_update_lds<false>(A, lda, i0, j0, A, lda, i0, k0, A, lda, k0, j0, smem);
   if (blockIdx.x == 0) {
+    // the diagonal tile's update lands in LDS, where its factorisation reads it
+    if (threadIdx.x < NB) smem[2 * NB * LS + NB + threadIdx.x] = 1e-12 * diag0[j0 + threadIdx.x];
+    tile_update_lds<false, false, true>(A, lda, i0, j0, A, lda, i0, k0, A, lda, k0, j0, smem);
     __syncthreads();
-    factor_diag(A, lda, k + 1, diag0, Dinv, flag, smem);
+    diag_factor_lds(A, lda, k + 1, Dinv, flag, smem);
+  } else {
+    tile_update_lds<false>(A, lda, i0, j0, A, lda, i0, k0, A, lda, k0, j0, smem);
   }
 }
 
