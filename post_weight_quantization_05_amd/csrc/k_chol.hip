@@ -62,6 +62,13 @@ __device__ __forceinline__ double readlane_f64(double v, int l) {
   return __hiloint2double(hi, lo);
 }
 
+// orders this wavefront's LDS accesses (its LDS operations complete in order)
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // 1 / sqrt(p) for p > 0: the hardware estimate refined by two Newton steps
 // y <- y (3 - p y^2) / 2 (each step squares the relative error).
 __device__ __forceinline__ double rsqrt_f64(double p) {
@@ -75,25 +82,53 @@ __device__ __forceinline__ double rsqrt_f64(double p) {
 // wavefronts, the block held in LDS and factored right-looking over four 16-column panels:
 //   (1) wavefront 0 factors the panel's rows c0 .. 63, one lane per row holding the row's
 //       16 panel entries in registers: per pivot j the pivot comes from lane j by readlane,
-//       each lane scales its own entry (L[i][j]) and updates its later entries with the
-//       column values L[c][j] read from lanes c by readlane.  The rows below the 16 x 16
-//       diagonal sub-block are solved by the same instructions;
+//       each lane scales its own entry (L[i][j]) and writes it to LDS, and updates its later
+//       entries with the column values L[c][j] (the next column's by readlane, the others
+//       read back from LDS at uniform addresses).  The rows below the 16 x 16 diagonal
+//       sub-block are solved by the same instructions;
 //   (2) all four wavefronts update the trailing lower triangle, A[i][j] -= sum over the
 //       panel of L[i][m] L[j][m], in 16 x 16 blocks on the matrix cores; one barrier
 //       before (2), one after.
-// The inverse: each wavefront inverts one 16 x 16 diagonal block of L by forward
-// substitution (one lane per column), then block forward substitution fills the blocks
-// below the diagonal.  Entries above the diagonal are never read as pivots or L entries
-// and are not stored.
+// The inverse X = L^{-1}, in 16 x 16 blocks: the diagonal blocks are formed inside (1), one
+// lane per column, by forward substitution; row block R below the diagonal,
+// X_Rq = -X_RR sum_{q <= m < R} L_Rm X_mq, by wavefronts 1 .. 3 on the matrix cores while
+// wavefront 0 runs the chain of panel R + 1 (the last row block after the loop).  Entries
+// above the diagonal are never read as pivots or L entries and are not stored.
 typedef double v4f64 __attribute__((ext_vector_type(4)));
 
 constexpr int PB = 16;                  // panel width
 constexpr int kDiagThreads = 256;
 constexpr int LS = NB + 1;              // LDS row stride of the block (doubles)
 
-// LDS of factor_diag, in doubles: the block (then L), X = L^{-1}, 1 / L[r][r], the pivot
-// tolerances and three 16 x 16 staging blocks of the block substitution.
-constexpr int kDiagLds = 2 * NB * LS + 2 * NB + 3 * PB * (PB + 1);
+// LDS of factor_diag, in doubles: the block (then L), X = L^{-1}, the pivot tolerances.
+constexpr int kTolOff = 2 * NB * LS;
+constexpr int kDiagLds = kTolOff + NB;
+
+// Row block R, column block q < R of X = L^{-1} (16 x 16 blocks, one wavefront):
+// X_Rq = -X_RR sum_{q <= m < R} L_Rm X_mq, with L in S and the blocks X_mq (m < R) and
+// X_RR already in Xf.  Both products run on v_mfma_f64_16x16x4; the second one's right
+// operand fragments are the first one's result registers (element i of lane l is row
+// l / 16 + 4 i, column l % 16, which is what step k = 4 i of the next product reads).
+__device__ __forceinline__ void x_offdiag(const double* S, double* Xf, int R, int q, int lane) {
+  const int lr = lane >> 4, lc = lane & 15;
+  v4f64 tb = v4f64{0.0, 0.0, 0.0, 0.0};
+  for (int m = q; m < R; ++m) {
+#pragma unroll
+    for (int k0 = 0; k0 < PB; k0 += 4) {
+      const double a = S[(PB * R + lc) * LS + PB * m + k0 + lr];
+      const double b = Xf[(PB * m + k0 + lr) * LS + PB * q + lc];
+      tb = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, tb, 0, 0, 0);
+    }
+  }
+  v4f64 xr = v4f64{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const double a = Xf[(PB * R + lc) * LS + PB * R + 4 * i + lr];
+    xr = __builtin_amdgcn_mfma_f64_16x16x4f64(a, tb[i], xr, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) Xf[(PB * R + lr + 4 * i) * LS + PB * q + lc] = -xr[i];
+}
 
 // Diagonal block k of A into S (the LDS block of factor_diag, lower part, zero above the
 // diagonal) and the pivot tolerances into tolv.  All 16 loads of a thread are in flight at
@@ -101,7 +136,7 @@ constexpr int kDiagLds = 2 * NB * LS + 2 * NB + 3 * PB * (PB + 1);
 __device__ __forceinline__ void diag_load(const double* __restrict__ A, int64_t lda, int64_t k,
                                           const double* __restrict__ diag0, double* smem) {
   double* S = smem;
-  double* tolv = smem + 2 * NB * LS + NB;
+  double* tolv = smem + kTolOff;
   const int tid = threadIdx.x;
   const int64_t k0 = k * NB;
   constexpr int PER = NB * NB / kDiagThreads;
@@ -127,9 +162,7 @@ __device__ __forceinline__ void diag_factor_lds(double* __restrict__ A, int64_t 
                                                 uint32_t* __restrict__ flag, double* smem) {
   double* S = smem;                           // the block, then L (lower)
   double* Xf = S + NB * LS;                   // X = L^{-1}
-  double* rinv = Xf + NB * LS;                // 1 / L[r][r]
-  double* tolv = rinv + NB;                   // 1e-12 of the original diagonal
-  double* Tb = tolv + NB;                     // [3][PB][PB + 1]
+  const double* tolv = smem + kTolOff;        // 1e-12 of the original diagonal
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int64_t k0 = k * NB;
@@ -137,11 +170,14 @@ __device__ __forceinline__ void diag_factor_lds(double* __restrict__ A, int64_t 
   bool notpd = false;
 #pragma unroll 1
   for (int c0 = 0; c0 < NB; c0 += PB) {
+    const int pb = c0 / PB;
     if (wave == 0) {
-      // (1) the panel's rows c0 .. 63, one lane per row, 16 entries in registers
+      // (1) the panel's rows c0 .. 63, one lane per row, 16 entries in registers; lane c < 16
+      // also forms column c of the inverse of the 16 x 16 diagonal sub-block, row j right
+      // after pivot j (row j of L is final then)
       const bool act = lane < NB - c0;
       const int i = c0 + (act ? lane : 0);
-      double v[PB];
+      double v[PB], x[PB];
 #pragma unroll
       for (int m = 0; m < PB; ++m) v[m] = act ? S[i * LS + c0 + m] : 0.0;
       const double tol = act ? tolv[i] : 0.0;
@@ -152,14 +188,26 @@ __device__ __forceinline__ void diag_factor_lds(double* __restrict__ A, int64_t 
         const double rj = rsqrt_f64(p > 0.0 ? p : 0.0);
         const double t = (act && lane >= j) ? v[j] * rj : 0.0;   // L[i][c0 + j]
         v[j] = t;
-        if (lane == 0) rinv[c0 + j] = rj;
+        if (act) S[i * LS + c0 + j] = t;                         // column j of L, in place
+        wave_sync_lds();
+        // the next pivot's column first; the other column values come back from LDS as
+        // uniform reads
+        if (j + 1 < PB) v[j + 1] = fma(-t, readlane_f64(t, j + 1), v[j + 1]);
 #pragma unroll
-        for (int c = j + 1; c < PB; ++c) v[c] = fma(-t, readlane_f64(t, c), v[c]);
-      }
-      if (act) {
+        for (int c = j + 2; c < PB; ++c) v[c] = fma(-t, S[(c0 + c) * LS + c0 + j], v[c]);
+        // row j of the sub-block's inverse, column `lane`: L[j][m] for m < j is final
+        double xa = (lane == j) ? 1.0 : 0.0;
 #pragma unroll
-        for (int m = 0; m < PB; ++m) S[i * LS + c0 + m] = v[m];
+        for (int m = 0; m < j; ++m) xa = fma(-S[(c0 + j) * LS + c0 + m], x[m], xa);
+        x[j] = (j >= lane) ? xa * rj : 0.0;
       }
+      if (lane < PB) {
+#pragma unroll
+        for (int r = 0; r < PB; ++r) Xf[(c0 + r) * LS + c0 + lane] = x[r];
+      }
+    } else if (wave < pb) {
+      // meanwhile: row block pb - 1 of the inverse, column block wave - 1
+      x_offdiag(S, Xf, pb - 1, wave - 1, lane);
     }
     __syncthreads();
     // (2) trailing lower triangle, rows and columns c0 + 16 .. 63, in 16 x 16 blocks on the
@@ -183,6 +231,8 @@ __device__ __forceinline__ void diag_factor_lds(double* __restrict__ A, int64_t 
     }
     __syncthreads();
   }
+  // the last row block of the inverse
+  if (wave < NB / PB - 1) x_offdiag(S, Xf, NB / PB - 1, wave, lane);
   if (__any(notpd) && tid == 0) atomicOr(flag, FLAG_NOTPD);
 
 #pragma unroll
@@ -191,58 +241,7 @@ __device__ __forceinline__ void diag_factor_lds(double* __restrict__ A, int64_t 
     const int i = e / NB, c = e % NB;
     if (c <= i) A[(k0 + i) * lda + k0 + c] = S[i * LS + c];
   }
-
-  // X = L^{-1}.  Diagonal blocks: wavefront w inverts block w, lane c < 16 forming column c
-  // by forward substitution, x[r] = (delta_rc - sum_{c<=m<r} L[r][m] x[m]) / L[r][r].
-  {
-    const int b0 = PB * wave;
-    if (lane < PB) {
-      double x[PB];
-#pragma unroll
-      for (int rr = 0; rr < PB; ++rr) {
-        double acc = (rr == lane) ? 1.0 : 0.0;
-#pragma unroll
-        for (int m = 0; m < rr; ++m) acc = fma(-S[(b0 + rr) * LS + b0 + m], x[m], acc);
-        x[rr] = (rr >= lane) ? acc * rinv[b0 + rr] : 0.0;
-      }
-#pragma unroll
-      for (int rr = 0; rr < PB; ++rr) Xf[(b0 + rr) * LS + b0 + lane] = x[rr];
-    }
-  }
   __syncthreads();
-  // blocks below the diagonal by block forward substitution: X_ip = -X_ii sum_{q=p}^{i-1}
-  // L_iq X_qp for p < i, one block row after the other (two barriers each); thread (a, b)
-  // owns entry (a, b) of every block
-  {
-    const int ea = tid >> 4, eb = tid & 15;
-#pragma unroll
-    for (int bi = 1; bi < NB / PB; ++bi) {
-#pragma unroll
-      for (int bp = 0; bp < bi; ++bp) {
-        double t0 = 0.0, t1 = 0.0;
-#pragma unroll
-        for (int bq = bp; bq < bi; ++bq)
-#pragma unroll
-          for (int m = 0; m < PB; m += 2) {
-            t0 = fma(S[(PB * bi + ea) * LS + PB * bq + m], Xf[(PB * bq + m) * LS + PB * bp + eb], t0);
-            t1 = fma(S[(PB * bi + ea) * LS + PB * bq + m + 1], Xf[(PB * bq + m + 1) * LS + PB * bp + eb], t1);
-          }
-        Tb[(bp * PB + ea) * (PB + 1) + eb] = t0 + t1;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int bp = 0; bp < bi; ++bp) {
-        double t0 = 0.0, t1 = 0.0;
-#pragma unroll
-        for (int m = 0; m < PB; m += 2) {
-          t0 = fma(Xf[(PB * bi + ea) * LS + PB * bi + m], Tb[(bp * PB + m) * (PB + 1) + eb], t0);
-          t1 = fma(Xf[(PB * bi + ea) * LS + PB * bi + m + 1], Tb[(bp * PB + m + 1) * (PB + 1) + eb], t1);
-        }
-        Xf[(PB * bi + ea) * LS + PB * bp + eb] = -(t0 + t1);
-      }
-      __syncthreads();
-    }
-  }
   double* __restrict__ out = Dinv + k * NB * NB;
 #pragma unroll
   for (int t = 0; t < NB * NB / kDiagThreads; ++t) {
@@ -415,7 +414,7 @@ __global__ __launch_bounds__(kThreads) void col_diag(double* __restrict__ A, int
   const int64_t i0 = j0 + static_cast<int64_t>(blockIdx.x) * NB, k0 = k * NB;
   if (blockIdx.x == 0) {
     // the diagonal tile's update lands in LDS, where its factorisation reads it
-    if (threadIdx.x < NB) smem[2 * NB * LS + NB + threadIdx.x] = 1e-12 * diag0[j0 + threadIdx.x];
+    if (threadIdx.x < NB) smem[kTolOff + threadIdx.x] = 1e-12 * diag0[j0 + threadIdx.x];
     tile_update_lds<false, false, true>(A, lda, i0, j0, A, lda, i0, k0, A, lda, k0, j0, smem);
     __syncthreads();
     diag_factor_lds(A, lda, k + 1, Dinv, flag, smem);
@@ -586,7 +585,7 @@ int factor_reversed(const float* H, int64_t d, const int32_t* perm, double* A, i
     if (X) QZ_TRY(fork(s_inv, la ? la->ev_panel : nullptr));
     if (below > 0) {
       if (k > 0) QZ_TRY(fork(s, la ? la->ev_trail : nullptr));   // rest update of k - 1 done
-      col_diag<<<static_cast<unsigned>(below), kThreads, 0, s>>>(A, dp, k, diag0, Dinv, flag);
+      col_diag<<<static_cast<unsigned>(below), kThreads, 30720, s>>>(A, dp, k, diag0, Dinv, flag);
       QZ_TRY(check_launch("rfactor.coldiag"));
     }
     if (below > 1) {
