@@ -29,7 +29,9 @@ namespace {
 constexpr int NB = 64;
 constexpr int kThreads = 256;
 
-// A[i][j] = Hp[d-1-i][d-1-j] (Hp = H[perm][:, perm]) for i, j < d; identity padding.
+// A[i][j] = Hp[d-1-i][d-1-j] (Hp = H[perm][:, perm]) for i, j < d; identity padding.  Only
+// the tiles on or below the diagonal are written (the factorisation reads no others); every
+// entry of H is still checked.
 __global__ __launch_bounds__(kThreads) void init_reversed(const float* __restrict__ H, int64_t d,
                                                           const int32_t* __restrict__ perm,
                                                           double* __restrict__ A, int64_t lda,
@@ -50,7 +52,7 @@ __global__ __launch_bounds__(kThreads) void init_reversed(const float* __restric
     } else {
       v = (i == j) ? 1.0 : 0.0;
     }
-    A[e] = v;
+    if (j / NB <= i / NB) A[e] = v;
     if (i == j) diag0[i] = v;
   }
   if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(flag, FLAG_NONFINITE);
@@ -440,21 +442,40 @@ __global__ __launch_bounds__(kThreads) void inv_update(double* __restrict__ X, i
   tile_update<true>(X, ldx, rb * NB, jb * NB, L, ldl, rb * NB, i * NB, X, ldx, i * NB, jb * NB);
 }
 
+// X = I on the tiles on or below the diagonal (the only ones the inverse reads).
 __global__ __launch_bounds__(kThreads) void fill_identity(double* __restrict__ X, int64_t ld) {
   const int64_t total = ld * ld;
   for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * blockDim.x)
-    X[e] = (e / ld == e % ld) ? 1.0 : 0.0;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i = e / ld, j = e % ld;
+    if (j / NB <= i / NB) X[e] = (i == j) ? 1.0 : 0.0;
+  }
 }
 
-// Rt[a][b] = R[b][a] = Linv[d-1-b][d-1-a] (zero above the diagonal), fp32.
+// Rt[a][b] = R[b][a] = Linv[d-1-b][d-1-a] (zero above the diagonal), fp32.  One 64 x 64
+// tile of Rt per workgroup (grid: column tiles x row tiles), transposed through LDS so that
+// both the reads of X and the writes of Rt are coalesced; tiles above the diagonal are only
+// zero-filled.
 __global__ __launch_bounds__(kThreads) void extract_rt(const double* __restrict__ X, int64_t ldx,
                                                        int64_t d, float* __restrict__ Rt, int64_t ldr) {
-  const int64_t total = d * d;
-  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t a = e / d, b = e % d;
-    Rt[a * ldr + b] = (b <= a) ? static_cast<float>(X[(d - 1 - b) * ldx + (d - 1 - a)]) : 0.0f;
+  __shared__ float t[NB][NB + 1];
+  const int64_t a0 = static_cast<int64_t>(blockIdx.y) * NB, b0 = static_cast<int64_t>(blockIdx.x) * NB;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  if (b0 <= a0) {
+#pragma unroll
+    for (int s = 0; s < NB / 4; ++s) {
+      const int by = ty + 4 * s;
+      const int64_t a = a0 + tx, b = b0 + by;
+      // X row d-1-b, column d-1-a: consecutive lanes read consecutive (descending) columns
+      t[by][tx] = (a < d && b < d && b <= a) ? static_cast<float>(X[(d - 1 - b) * ldx + (d - 1 - a)]) : 0.0f;
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int s = 0; s < NB / 4; ++s) {
+    const int ay = ty + 4 * s;
+    const int64_t a = a0 + ay, b = b0 + tx;
+    if (a < d && b < d) Rt[a * ldr + b] = (b0 <= a0) ? t[tx][ay] : 0.0f;
   }
 }
 
@@ -487,7 +508,8 @@ struct Lookahead {
   int device = -1;
   bool ok = false;
   hipStream_t trail = nullptr, inv = nullptr;
-  hipEvent_t ev_panel = nullptr, ev_trail = nullptr, ev_join1 = nullptr, ev_join2 = nullptr;
+  hipEvent_t ev_start = nullptr, ev_panel = nullptr, ev_trail = nullptr, ev_join1 = nullptr,
+            ev_join2 = nullptr;
   hipStream_t side = nullptr;                        // work beside the factorisation
   hipEvent_t ev_fork = nullptr, ev_back = nullptr;
 };
@@ -503,6 +525,7 @@ Lookahead* lookahead() {
   l.ok = hipStreamCreateWithFlags(&l.trail, hipStreamNonBlocking) == hipSuccess &&
          hipStreamCreateWithFlags(&l.inv, hipStreamNonBlocking) == hipSuccess &&
          hipStreamCreateWithFlags(&l.side, hipStreamNonBlocking) == hipSuccess &&
+         hipEventCreateWithFlags(&l.ev_start, hipEventDisableTiming) == hipSuccess &&
          hipEventCreateWithFlags(&l.ev_panel, hipEventDisableTiming) == hipSuccess &&
          hipEventCreateWithFlags(&l.ev_trail, hipEventDisableTiming) == hipSuccess &&
          hipEventCreateWithFlags(&l.ev_join1, hipEventDisableTiming) == hipSuccess &&
@@ -566,12 +589,16 @@ int factor_reversed(const float* H, int64_t d, const int32_t* perm, double* A, i
     QZ_HIP(hipEventRecord(ev, on));
     return QZ_OK;
   };
-  init_reversed<<<grid_for(dp * dp), kThreads, 0, s>>>(H, d, perm, A, dp, diag0, flag);
-  QZ_TRY(check_launch("rfactor.init"));
   if (X) {
-    fill_identity<<<grid_for(dp * dp), kThreads, 0, s>>>(X, dp);
+    // X = I on the inverse's stream, beside the init (after all earlier work on s, which
+    // may still read X)
+    QZ_TRY(mark(la ? la->ev_start : nullptr, s));
+    QZ_TRY(fork(s_inv, la ? la->ev_start : nullptr));
+    fill_identity<<<grid_for(dp * dp), kThreads, 0, s_inv>>>(X, dp);
     QZ_TRY(check_launch("rfactor.fill"));
   }
+  init_reversed<<<grid_for(dp * dp), kThreads, 0, s>>>(H, d, perm, A, dp, diag0, flag);
+  QZ_TRY(check_launch("rfactor.init"));
   diag_block_panels<<<1, kDiagThreads, 0, s>>>(A, dp, 0, diag0, Dinv, flag);
   QZ_TRY(check_launch("rfactor.diag"));
   for (int64_t k = 0; k < nblk; ++k) {
@@ -637,7 +664,8 @@ int rfactor_enqueue(const float* H, int64_t d, const int32_t* perm, float* Rt, i
   double* Dinv = cv.take<double>(static_cast<size_t>(nblk) * NB * NB);
   double* diag0 = cv.take<double>(static_cast<size_t>(dp));
   QZ_TRY(factor_reversed(H, d, perm, A, dp, Dinv, diag0, X, flag, s));
-  extract_rt<<<grid_for(d * d), kThreads, 0, s>>>(X, dp, d, Rt, ldr);
+  const unsigned nt = static_cast<unsigned>(ceil_div(d, NB));
+  extract_rt<<<dim3(nt, nt), kThreads, 0, s>>>(X, dp, d, Rt, ldr);
   return check_launch("rfactor.extract");
 }
 
