@@ -29,19 +29,22 @@ namespace {
 constexpr int NB = 64;
 constexpr int kThreads = 256;
 
-// A[i][j] = Hp[d-1-i][d-1-j] (Hp = H[perm][:, perm]) for i, j < d; identity padding.  Only
-// the tiles on or below the diagonal are written (the factorisation reads no others); every
-// entry of H is still checked.
+// A[i][j] = Hp[d-1-i][d-1-j] (Hp = H[perm][:, perm]) for i, j < d, identity padding, over
+// the block columns jb0 <= j / 64 < jb1 (all rows).  Only the tiles on or below the diagonal
+// are written (the factorisation reads no others); every entry of H in those columns is
+// checked.
 __global__ __launch_bounds__(kThreads) void init_reversed(const float* __restrict__ H, int64_t d,
                                                           const int32_t* __restrict__ perm,
                                                           double* __restrict__ A, int64_t lda,
+                                                          int64_t jb0, int64_t jb1,
                                                           double* __restrict__ diag0,
                                                           uint32_t* __restrict__ flag) {
-  const int64_t total = lda * lda;
+  const int64_t w = (jb1 - jb0) * NB;
+  const int64_t total = lda * w;
   bool bad = false;
   for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
        e += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t i = e / lda, j = e % lda;
+    const int64_t i = e / w, j = jb0 * NB + e % w;
     double v;
     if (i < d && j < d) {
       int64_t si = d - 1 - i, sj = d - 1 - j;
@@ -52,7 +55,7 @@ __global__ __launch_bounds__(kThreads) void init_reversed(const float* __restric
     } else {
       v = (i == j) ? 1.0 : 0.0;
     }
-    if (j / NB <= i / NB) A[e] = v;
+    if (j / NB <= i / NB) A[i * lda + j] = v;
     if (i == j) diag0[i] = v;
   }
   if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(flag, FLAG_NONFINITE);
@@ -102,7 +105,8 @@ constexpr int PB = 16;                  // panel width
 constexpr int kDiagThreads = 256;
 constexpr int LS = NB + 1;              // LDS row stride of the block (doubles)
 
-// LDS of factor_diag, in doubles: the block (then L), X = L^{-1}, the pivot tolerances.
+// LDS of the diagonal factorisation, in doubles: the block (then L), X = L^{-1}, the pivot
+// tolerances.
 constexpr int kTolOff = 2 * NB * LS;
 constexpr int kDiagLds = kTolOff + NB;
 
@@ -132,7 +136,7 @@ __device__ __forceinline__ void x_offdiag(const double* S, double* Xf, int R, in
   for (int i = 0; i < 4; ++i) Xf[(PB * R + lr + 4 * i) * LS + PB * q + lc] = -xr[i];
 }
 
-// Diagonal block k of A into S (the LDS block of factor_diag, lower part, zero above the
+// Diagonal block k of A into S (the LDS block of the factorisation, lower part, zero above the
 // diagonal) and the pivot tolerances into tolv.  All 16 loads of a thread are in flight at
 // once (every address lies inside A).
 __device__ __forceinline__ void diag_load(const double* __restrict__ A, int64_t lda, int64_t k,
@@ -252,25 +256,6 @@ __device__ __forceinline__ void diag_factor_lds(double* __restrict__ A, int64_t 
     out[e] = (rr >= cc) ? Xf[rr * LS + cc] : 0.0;
   }
 }
-
-__device__ __forceinline__ void factor_diag(double* __restrict__ A, int64_t lda, int64_t k,
-                                            const double* __restrict__ diag0,
-                                            double* __restrict__ Dinv, uint32_t* __restrict__ flag,
-                                            double* smem) {
-  diag_load(A, lda, k, diag0, smem);
-  __syncthreads();
-  diag_factor_lds(A, lda, k, Dinv, flag, smem);
-}
-
-__global__ __launch_bounds__(kDiagThreads) void diag_block_panels(double* __restrict__ A, int64_t lda,
-                                                                  int64_t k,
-                                                                  const double* __restrict__ diag0,
-                                                                  double* __restrict__ Dinv,
-                                                                  uint32_t* __restrict__ flag) {
-  __shared__ double smem[kDiagLds];
-  factor_diag(A, lda, k, diag0, Dinv, flag, smem);
-}
-
 
 __device__ __forceinline__ void tri_tile(int64_t t, int64_t& ti, int64_t& tj) {
   // lower-triangle enumeration: (0,0), (1,0), (1,1), (2,0), ...
@@ -404,8 +389,13 @@ __global__ __launch_bounds__(kThreads) void panel_solve(double* __restrict__ A, 
 
 // The update of block column k + 1 by panel k, A(i,k+1) -= L(i,k) L(k+1,k)^T for the block
 // rows i > k, and then, in workgroup 0 (whose tile is the next diagonal block), the
-// factorisation and inverse of diagonal block k + 1: one launch on the critical chain.
+// factorisation and inverse of diagonal block k + 1: one launch on the critical chain.  With
+// k = -1 (one workgroup) it only factors diagonal block 0, read from A.
 constexpr int kStepLds = (kDiagLds > 2 * NB * (NB + 1)) ? kDiagLds : 2 * NB * (NB + 1);
+// Extra dynamic LDS for this launch: with it, no workgroup of the 64 x 64 tile kernels
+// (66.5 KB each) fits on the compute unit beside the diagonal factorisation, which
+// therefore runs alone on its unit.
+constexpr size_t kStepPadBytes = 30720;
 
 __global__ __launch_bounds__(kThreads) void col_diag(double* __restrict__ A, int64_t lda, int64_t k,
                                                      const double* __restrict__ diag0,
@@ -415,9 +405,13 @@ __global__ __launch_bounds__(kThreads) void col_diag(double* __restrict__ A, int
   const int64_t j0 = (k + 1) * NB;
   const int64_t i0 = j0 + static_cast<int64_t>(blockIdx.x) * NB, k0 = k * NB;
   if (blockIdx.x == 0) {
-    // the diagonal tile's update lands in LDS, where its factorisation reads it
-    if (threadIdx.x < NB) smem[kTolOff + threadIdx.x] = 1e-12 * diag0[j0 + threadIdx.x];
-    tile_update_lds<false, false, true>(A, lda, i0, j0, A, lda, i0, k0, A, lda, k0, j0, smem);
+    if (k < 0) {
+      diag_load(A, lda, 0, diag0, smem);
+    } else {
+      // the diagonal tile's update lands in LDS, where its factorisation reads it
+      if (threadIdx.x < NB) smem[kTolOff + threadIdx.x] = 1e-12 * diag0[j0 + threadIdx.x];
+      tile_update_lds<false, false, true>(A, lda, i0, j0, A, lda, i0, k0, A, lda, k0, j0, smem);
+    }
     __syncthreads();
     diag_factor_lds(A, lda, k + 1, Dinv, flag, smem);
   } else {
@@ -589,17 +583,26 @@ int factor_reversed(const float* H, int64_t d, const int32_t* perm, double* A, i
     QZ_HIP(hipEventRecord(ev, on));
     return QZ_OK;
   };
+  // The side streams start after all earlier work on s (which may still read A or X).  The
+  // chain needs block columns 0 and 1 of A first; the init of the others runs on the rest
+  // update's stream, ahead of the first rest update, and X = I on the inverse's stream.
+  QZ_TRY(mark(la ? la->ev_start : nullptr, s));
+  QZ_TRY(fork(s_trail, la ? la->ev_start : nullptr));
   if (X) {
-    // X = I on the inverse's stream, beside the init (after all earlier work on s, which
-    // may still read X)
-    QZ_TRY(mark(la ? la->ev_start : nullptr, s));
     QZ_TRY(fork(s_inv, la ? la->ev_start : nullptr));
     fill_identity<<<grid_for(dp * dp), kThreads, 0, s_inv>>>(X, dp);
     QZ_TRY(check_launch("rfactor.fill"));
   }
-  init_reversed<<<grid_for(dp * dp), kThreads, 0, s>>>(H, d, perm, A, dp, diag0, flag);
+  const int64_t near = nblk < 2 ? nblk : 2;
+  init_reversed<<<grid_for(dp * near * NB), kThreads, 0, s>>>(H, d, perm, A, dp, 0, near, diag0,
+                                                              flag);
   QZ_TRY(check_launch("rfactor.init"));
-  diag_block_panels<<<1, kDiagThreads, 0, s>>>(A, dp, 0, diag0, Dinv, flag);
+  if (nblk > near) {
+    init_reversed<<<grid_for(dp * (nblk - near) * NB), kThreads, 0, s_trail>>>(
+        H, d, perm, A, dp, near, nblk, diag0, flag);
+    QZ_TRY(check_launch("rfactor.init2"));
+  }
+  col_diag<<<1, kThreads, kStepPadBytes, s>>>(A, dp, -1, diag0, Dinv, flag);
   QZ_TRY(check_launch("rfactor.diag"));
   for (int64_t k = 0; k < nblk; ++k) {
     const int64_t below = nblk - k - 1;
@@ -612,7 +615,8 @@ int factor_reversed(const float* H, int64_t d, const int32_t* perm, double* A, i
     if (X) QZ_TRY(fork(s_inv, la ? la->ev_panel : nullptr));
     if (below > 0) {
       if (k > 0) QZ_TRY(fork(s, la ? la->ev_trail : nullptr));   // rest update of k - 1 done
-      col_diag<<<static_cast<unsigned>(below), kThreads, 30720, s>>>(A, dp, k, diag0, Dinv, flag);
+      col_diag<<<static_cast<unsigned>(below), kThreads, kStepPadBytes, s>>>(A, dp, k, diag0, Dinv,
+                                                                           flag);
       QZ_TRY(check_launch("rfactor.coldiag"));
     }
     if (below > 1) {
