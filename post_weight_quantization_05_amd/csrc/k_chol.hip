@@ -377,14 +377,31 @@ __global__ __launch_bounds__(kThreads) void chol_trailing(double* __restrict__ A
   tile_update<false>(A, lda, i0, j0, A, lda, i0, k0, A, lda, k0, j0);
 }
 
-// Rows below block k:  A[i][k-block] <- A[i][k-block] * Dinv_k^T.  One 64-row tile
-// per workgroup.
+// Rows below block k:  A[i][k-block] <- A[i][k-block] * Dinv_k^T, in place.  16 rows per
+// workgroup, one 16 x 16 output block per wavefront (16 v_mfma_f64_16x16x4 along K), the
+// fragments read straight from global memory (A_op[m][q] from row r0 + m, B_op[q][n] =
+// Dinv_k[n][q]), with the fragment layout and K order of tile_update_lds, so the results are
+// those of the 64-row tile product.  Every wavefront reads all 64 columns of the rows before
+// any wavefront writes its 16.
 __global__ __launch_bounds__(kThreads) void panel_solve(double* __restrict__ A, int64_t lda, int64_t k,
                                                         const double* __restrict__ Dinv) {
   const int64_t k0 = k * NB;
-  const int64_t r0 = k0 + NB + static_cast<int64_t>(blockIdx.x) * NB;
-  // out[i][c] = sum_q A[r0+i][k0+q] Dinv_k[c][q]
-  tile_update<false, true>(A, lda, r0, k0, A, lda, r0, k0, Dinv + k * NB * NB, NB, 0, 0);
+  const int64_t r0 = k0 + NB + static_cast<int64_t>(blockIdx.x) * 16;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lr = lane >> 4, lc = lane & 15;
+  const double* __restrict__ Dk = Dinv + k * NB * NB;
+  double a[NB / 4], b[NB / 4];
+#pragma unroll
+  for (int s = 0; s < NB / 4; ++s) {
+    a[s] = A[(r0 + lc) * lda + k0 + 4 * s + lr];
+    b[s] = Dk[(16 * w + lc) * NB + 4 * s + lr];
+  }
+  v4f64 acc = v4f64{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int s = 0; s < NB / 4; ++s) acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s], b[s], acc, 0, 0, 0);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) A[(r0 + lr + 4 * i) * lda + k0 + 16 * w + lc] = acc[i];
 }
 
 // The update of block column k + 1 by panel k, A(i,k+1) -= L(i,k) L(k+1,k)^T for the block
@@ -607,7 +624,7 @@ int factor_reversed(const float* H, int64_t d, const int32_t* perm, double* A, i
   for (int64_t k = 0; k < nblk; ++k) {
     const int64_t below = nblk - k - 1;
     if (below > 0) {
-      panel_solve<<<static_cast<unsigned>(below), kThreads, 0, s>>>(A, dp, k, Dinv);
+      panel_solve<<<static_cast<unsigned>(4 * below), kThreads, 0, s>>>(A, dp, k, Dinv);
       QZ_TRY(check_launch("rfactor.panel"));
     }
     QZ_TRY(mark(la ? la->ev_panel : nullptr, s));
