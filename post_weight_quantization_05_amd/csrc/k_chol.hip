@@ -106,9 +106,30 @@ constexpr int kDiagThreads = 256;
 constexpr int LS = NB + 1;              // LDS row stride of the block (doubles)
 
 // LDS of the diagonal factorisation, in doubles: the block (then L), X = L^{-1}, the pivot
-// tolerances.
+// tolerances and the reciprocal pivots.
 constexpr int kTolOff = 2 * NB * LS;
-constexpr int kDiagLds = kTolOff + NB;
+constexpr int kRinvOff = kTolOff + NB;   // 1 / L[r][r]
+constexpr int kDiagLds = kRinvOff + NB;
+
+// Diagonal block R of X = L^{-1} (16 x 16, one wavefront, lane c < 16 forming column c by
+// forward substitution: x[r] = (delta_rc - sum_{m<r} L[r][m] x[m]) / L[r][r]).  The same
+// operations in the same order as the form inside the pivot chain.
+__device__ __forceinline__ void x_diag(const double* S, double* Xf, const double* rinv, int R,
+                                       int lane) {
+  if (lane < PB) {
+    const int b0 = PB * R;
+    double x[PB];
+#pragma unroll
+    for (int r = 0; r < PB; ++r) {
+      double xa = (r == lane) ? 1.0 : 0.0;
+#pragma unroll
+      for (int m = 0; m < r; ++m) xa = fma(-S[(b0 + r) * LS + b0 + m], x[m], xa);
+      x[r] = (r >= lane) ? xa * rinv[b0 + r] : 0.0;
+    }
+#pragma unroll
+    for (int r = 0; r < PB; ++r) Xf[(b0 + r) * LS + b0 + lane] = x[r];
+  }
+}
 
 // Row block R, column block q < R of X = L^{-1} (16 x 16 blocks, one wavefront):
 // X_Rq = -X_RR sum_{q <= m < R} L_Rm X_mq, with L in S and the blocks X_mq (m < R) and
@@ -174,13 +195,15 @@ __device__ __forceinline__ void diag_factor_lds(double* __restrict__ A, int64_t 
   const int64_t k0 = k * NB;
 
   bool notpd = false;
+  double* rinv = smem + kRinvOff;
 #pragma unroll 1
   for (int c0 = 0; c0 < NB; c0 += PB) {
     const int pb = c0 / PB;
+    const bool last = c0 + PB == NB;
     if (wave == 0) {
-      // (1) the panel's rows c0 .. 63, one lane per row, 16 entries in registers; lane c < 16
-      // also forms column c of the inverse of the 16 x 16 diagonal sub-block, row j right
-      // after pivot j (row j of L is final then)
+      // (1) the panel's rows c0 .. 63, one lane per row, 16 entries in registers; in the last
+      // panel lane c < 16 also forms column c of the inverse of the 16 x 16 diagonal
+      // sub-block, row j right after pivot j (row j of L is final then)
       const bool act = lane < NB - c0;
       const int i = c0 + (act ? lane : 0);
       double v[PB], x[PB];
@@ -195,25 +218,30 @@ __device__ __forceinline__ void diag_factor_lds(double* __restrict__ A, int64_t 
         const double t = (act && lane >= j) ? v[j] * rj : 0.0;   // L[i][c0 + j]
         v[j] = t;
         if (act) S[i * LS + c0 + j] = t;                         // column j of L, in place
+        if (lane == 0) rinv[c0 + j] = rj;
         wave_sync_lds();
         // the next pivot's column first; the other column values come back from LDS as
         // uniform reads
         if (j + 1 < PB) v[j + 1] = fma(-t, readlane_f64(t, j + 1), v[j + 1]);
 #pragma unroll
         for (int c = j + 2; c < PB; ++c) v[c] = fma(-t, S[(c0 + c) * LS + c0 + j], v[c]);
-        // row j of the sub-block's inverse, column `lane`: L[j][m] for m < j is final
-        double xa = (lane == j) ? 1.0 : 0.0;
+        if (last) {
+          double xa = (lane == j) ? 1.0 : 0.0;
 #pragma unroll
-        for (int m = 0; m < j; ++m) xa = fma(-S[(c0 + j) * LS + c0 + m], x[m], xa);
-        x[j] = (j >= lane) ? xa * rj : 0.0;
+          for (int m = 0; m < j; ++m) xa = fma(-S[(c0 + j) * LS + c0 + m], x[m], xa);
+          x[j] = (j >= lane) ? xa * rj : 0.0;
+        }
       }
-      if (lane < PB) {
+      if (last && lane < PB) {
 #pragma unroll
         for (int r = 0; r < PB; ++r) Xf[(c0 + r) * LS + c0 + lane] = x[r];
       }
-    } else if (wave < pb) {
-      // meanwhile: row block pb - 1 of the inverse, column block wave - 1
-      x_offdiag(S, Xf, pb - 1, wave - 1, lane);
+    } else if (wave == 1) {
+      // meanwhile: the previous panel's diagonal block of the inverse
+      if (pb >= 1) x_diag(S, Xf, rinv, pb - 1, lane);
+    } else if (wave - 2 < pb - 2) {
+      // and row block pb - 2 of the inverse, column block wave - 2
+      x_offdiag(S, Xf, pb - 2, wave - 2, lane);
     }
     __syncthreads();
     // (2) trailing lower triangle, rows and columns c0 + 16 .. 63, in 16 x 16 blocks on the
@@ -237,6 +265,10 @@ __device__ __forceinline__ void diag_factor_lds(double* __restrict__ A, int64_t 
     }
     __syncthreads();
   }
+  // the last two row blocks of the inverse: row block 2 (its diagonal block came from the
+  // last panel's phase), then row block 3 (its diagonal block from the last chain)
+  if (wave >= 2) x_offdiag(S, Xf, NB / PB - 2, wave - 2, lane);
+  __syncthreads();
   // the last row block of the inverse
   if (wave < NB / PB - 1) x_offdiag(S, Xf, NB / PB - 1, wave, lane);
   if (__any(notpd) && tid == 0) atomicOr(flag, FLAG_NOTPD);
