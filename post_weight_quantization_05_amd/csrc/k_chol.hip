@@ -94,11 +94,13 @@ __device__ __forceinline__ double rsqrt_f64(double p) {
 //   (2) all four wavefronts update the trailing lower triangle, A[i][j] -= sum over the
 //       panel of L[i][m] L[j][m], in 16 x 16 blocks on the matrix cores; one barrier
 //       before (2), one after.
-// The inverse X = L^{-1}, in 16 x 16 blocks: the diagonal blocks are formed inside (1), one
-// lane per column, by forward substitution; row block R below the diagonal,
-// X_Rq = -X_RR sum_{q <= m < R} L_Rm X_mq, by wavefronts 1 .. 3 on the matrix cores while
-// wavefront 0 runs the chain of panel R + 1 (the last row block after the loop).  Entries
-// above the diagonal are never read as pivots or L entries and are not stored.
+// The inverse X = L^{-1}, in 16 x 16 blocks, formed by the other wavefronts while wavefront
+// 0 runs the next panel's chain: the diagonal block of panel p by wavefront 1 during chain
+// p + 1 (one lane per column, forward substitution; the last panel's by wavefront 0 inside
+// its own chain), row block R below the diagonal, X_Rq = -X_RR sum_{q <= m < R} L_Rm X_mq,
+// by wavefronts 2 and 3 on the matrix cores during chain R + 2 (row blocks 2 and 3 after
+// the loop).  Entries above the diagonal are never read as pivots or L entries and are
+// not stored.
 typedef double v4f64 __attribute__((ext_vector_type(4)));
 
 constexpr int PB = 16;                  // panel width
