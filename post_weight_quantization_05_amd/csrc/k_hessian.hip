@@ -305,19 +305,27 @@ __global__ __launch_bounds__(kThreads, 1) void gram_bf16_dma_kernel(const HArgs 
 
 // vmcnt(0) (the pair's DMA landed) and lgkmcnt(0) (zero fills and this wave's LDS reads
 // done), then the workgroup barrier.  s_waitcnt 0x0070: vmcnt 0, expcnt 7, lgkmcnt 0.
+// The stage count is rounded up to even (a stage past the token range is zero-filled and
+// adds nothing), so both stages of a pair run without a branch between them and the
+// compiler can read the second stage's operands while the first stage's MFMAs run.
 #define QZ_PAIR(kk, C0, C1, N0, N1)                                                        \
-  if ((kk) < nk) {                                                                         \
+  if ((kk) < nke) {                                                                        \
     __builtin_amdgcn_s_waitcnt(0x0070);                                                    \
     __builtin_amdgcn_s_barrier();                                                          \
-    if ((kk) + 2 < nk) QZ_ISSUE(N0, (kk) + 2);                                             \
-    if ((kk) + 3 < nk) QZ_ISSUE(N1, (kk) + 3);                                             \
+    if ((kk) + 2 < nke) {                                                                  \
+      QZ_ISSUE(N0, (kk) + 2);                                                              \
+      QZ_ISSUE(N1, (kk) + 3);                                                              \
+    }                                                                                      \
     QZ_COMPUTE(C0)                                                                         \
-    if ((kk) + 1 < nk) QZ_COMPUTE(C1)                                                      \
+    QZ_COMPUTE(C1)                                                                         \
   }
 
-  if (0 < nk) QZ_ISSUE(L0, 0);
-  if (1 < nk) QZ_ISSUE(L1, 1);
-  for (int64_t kt = 0; kt < nk; kt += NSTAGE) {
+  const int64_t nke = nk + (nk & 1);
+  if (0 < nke) {
+    QZ_ISSUE(L0, 0);
+    QZ_ISSUE(L1, 1);
+  }
+  for (int64_t kt = 0; kt < nke; kt += NSTAGE) {
     QZ_PAIR(kt + 0, L0, L1, L2, L3)
     QZ_PAIR(kt + 2, L2, L3, L0, L1)
   }
