@@ -10,7 +10,11 @@
 // cannot fill the chip).  X streams from HBM into LDS with global_load_lds (no register
 // round trip), token-major with a chunk swizzle, and ds_read_b64_tr_b16 hands every lane
 // the 8 consecutive tokens of one channel that v_mfma_f32_32x32x16_bf16 wants per
-// operand (the transpose happens in the LDS read).  bf16 x bf16 products are exact in
+// operand (the transpose happens in the LDS read); the operands of the next 16-token
+// step are read while the matrix cores work through the current one.  What bounds the
+// kernel is the stream of X into LDS (the copies alone, with no operand reads, take ~90%
+// of the kernel's time), so the tile is as large as the fp32 accumulators allow and the
+// work is dealt so that concurrently resident tiles share panels in L2.  bf16 x bf16 products are exact in
 // fp32; sums accumulate in fp32 in the MFMA.  X whose rows are not 16-byte aligned goes
 // through a kernel that stages the same token-major tiles with register loads (element
 // loads at the ragged edge) instead of the direct copies.
@@ -36,6 +40,7 @@ constexpr int HT = 256;          // output tile edge
 constexpr int HBK = 32;          // tokens per pipeline stage
 constexpr int LDR = HT + 32;     // LDS row (one token) in bf16: 576 bytes, rows 16 banks apart
 constexpr int kThreads = 512;    // 8 wavefronts: 4 (rows) x 2 (columns), 64 x 128 each
+constexpr int64_t kSlots = 256;  // resident workgroups of the main kernel: one per CU
 
 struct HArgs {
   const uint16_t* X;
@@ -242,25 +247,58 @@ __device__ __forceinline__ void dma_panel(uint16_t* dst, const uint16_t* __restr
   }
 }
 
-// Pipeline: four stage buffers used as two pairs.  After one barrier the wavefronts
-// issue the DMA of the next pair of stages (into the pair consumed before the barrier)
-// and then run the matrix cores over the current pair (64 tokens: 32 MFMAs per
-// wavefront); the next barrier first waits for that DMA.  One barrier per 64 tokens
-// keeps the two wavefronts of a SIMD from stalling in lock-step on every 32 tokens.
+// Stage copy: lane l of wavefront w copies, for each of the two row halves (rep), token
+// row 2w + l/32 + 16 rep and the 16-byte piece that lands at byte 16 (l mod 32) of that
+// LDS row under the chunk swizzle.  The source is a wave-uniform base in scalar
+// registers plus one 32-bit lane offset that is the same for every stage and panel.  In
+// a stage that lies wholly inside X every lane copies; otherwise lanes whose token row is
+// at or past k_end, or whose 8 channels are at or past d, write zeros instead (with
+// d % 8 == 0 a 16-byte piece is wholly inside or wholly outside).
+__device__ __forceinline__ void dma_row(uint16_t* dst_row, const uint16_t* src, uint32_t voff) {
+  const uint32_t lds_off = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint16_t*)dst_row)));
+  // The base must sit in scalar registers (the instruction's saddr operand); it is
+  // wave-uniform, and readfirstlane makes that explicit to the compiler.
+  const uint64_t sa = reinterpret_cast<uint64_t>(src);
+  // (readfirstlane returns int: each half goes through uint32_t so that widening the
+  // low half cannot sign-extend into the high half.)
+  const uint32_t s_lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(sa)));
+  const uint32_t s_hi =
+      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(sa >> 32)));
+  const uint64_t su = (static_cast<uint64_t>(s_hi) << 32) | s_lo;
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_off), "v"(voff), "s"(reinterpret_cast<const uint16_t*>(su))
+               : "memory", "m0");
+}
+
+// Pipeline: four stage buffers used as two pairs (64 tokens each); operands are
+// double-buffered in registers, so the transposing LDS reads for the next 16-token
+// step are in flight while the matrix cores work through the current one.  One
+// barrier per pair, placed before the pair's last step (whose operands are already in
+// registers): once every wavefront has passed it, the pair's buffers are free for the
+// copies of the pair after next, and the next pair's copies (waited for just before the
+// barrier) are visible, so its first operands are read before the last step's MFMAs;
+// the copies of the pair after next are issued behind those MFMAs.
 __global__ __launch_bounds__(kThreads, 1) void gram_bf16_dma_kernel(const HArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t L0[2 * PANEL];
-  __shared__ __attribute__((aligned(16))) uint16_t L1[2 * PANEL];
-  __shared__ __attribute__((aligned(16))) uint16_t L2[2 * PANEL];
-  __shared__ __attribute__((aligned(16))) uint16_t L3[2 * PANEL];
+  __shared__ __attribute__((aligned(16))) uint16_t Ls[NSTAGE * 2 * PANEL];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
+  // Work items in split-major order, dealt per round of kSlots resident workgroups: the
+  // hardware deals workgroups round-robin to the 8 XCDs, so within each full round the
+  // logical ids are regrouped to give every XCD 32 consecutive items (a compact group of
+  // tiles, sharing panels through that XCD's L2), while all XCDs stay on the same one or
+  // two token splits (sharing them in the last-level cache and in DRAM pages).
   int64_t pid = blockIdx.x;
   const int64_t nblk = gridDim.x;
-  if ((nblk & 7) == 0) pid = (pid & 7) * (nblk >> 3) + (pid >> 3);
+  {
+    const int64_t r = pid / kSlots, in = pid % kSlots;
+    if ((r + 1) * kSlots <= nblk) pid = r * kSlots + (in & 7) * (kSlots / 8) + (in >> 3);
+  }
   const int64_t split = pid / g.n_tiles, t = pid % g.n_tiles;
   const int64_t I = g.tiles[2 * t], J = g.tiles[2 * t + 1];
   const bool diag = (I == J);
@@ -268,9 +306,38 @@ __global__ __launch_bounds__(kThreads, 1) void gram_bf16_dma_kernel(const HArgs 
   const int64_t k_begin = split * g.chunk;
   int64_t k_end = k_begin + g.chunk;
   if (k_end > g.n) k_end = g.n;
-  const uint16_t* __restrict__ X = g.X;
   const int64_t d = g.d;
   const int64_t nk = (k_end > k_begin) ? ceil_div(k_end - k_begin, HBK) : 0;
+  const int64_t np = (nk + 1) >> 1;   // pairs; a stage past the token range is zero-filled
+  const bool cols_in = (i0 + HT <= d) && (j0 + HT <= d);
+
+  // Copy roles (see dma_row).
+  const int crow = 2 * wave + (lane >> 5);
+  const int cq = lane & 31;
+  const int ccol = 16 * ((cq >> 1) ^ (2 * (crow & 3))) + 8 * (cq & 1);
+  const uint32_t voff = static_cast<uint32_t>((crow * d + ccol) * sizeof(uint16_t));
+  const bool a_col = i0 + ccol < d, b_col = j0 + ccol < d;
+  const uint16_t* __restrict__ xa = g.X + k_begin * d + i0;   // token k_begin, channel i0
+  const int64_t jdelta = j0 - i0;
+
+  // Operand roles: byte offsets into Ls of the first transposing read of each operand
+  // (stage buffer 0, tokens 0..3 of the step); the other reads add immediates.
+  uint32_t aoff[2], boffs[4];
+  {
+    const int gq = lane >> 4, s = lane & 15;
+    const int kl = 8 * (gq >> 1) + (s >> 2);
+    const int ml = 16 * (gq & 1) + 4 * (s & 3);
+    auto sw = [&](int m) {
+      return static_cast<uint32_t>(2 * (kl * HT + 16 * ((m >> 4) ^ (2 * (kl & 3))) + (m & 15)));
+    };
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) aoff[mt] = sw(wm * 64 + mt * 32 + ml);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+      boffs[nt] = sw(wn * 128 + nt * 32 + ml) + (diag ? 0u : 2u * PANEL);
+  }
+  typedef __attribute__((address_space(3))) char lds_char;
+  lds_char* const lbase = (lds_char*)(__attribute__((address_space(3))) uint16_t*)Ls;
 
   f32x16 acc[2][4];
 #pragma unroll
@@ -280,57 +347,97 @@ __global__ __launch_bounds__(kThreads, 1) void gram_bf16_dma_kernel(const HArgs 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-#define QZ_ISSUE(BUF, kk)                                                                  \
+  bf16x8 ra0[2], rb0[4], ra1[2], rb1[4];
+
+#define QZ_ISSUE(BUF, st)                                                                  \
   do {                                                                                     \
-    dma_panel(BUF, X, k_begin + (kk) * HBK, k_end, i0, d, wave, lane);                     \
-    if (!diag) dma_panel(BUF + PANEL, X, k_begin + (kk) * HBK, k_end, j0, d, wave, lane);  \
+    const int64_t kr_ = (st) * HBK;   /* first token row of the stage, from k_begin */     \
+    uint16_t* dst_ = Ls + (BUF) * 2 * PANEL;                                               \
+    const bool full_ = cols_in && k_begin + kr_ + HBK <= k_end;                            \
+    _Pragma("unroll") for (int rep = 0; rep < 2; ++rep) {                                  \
+      const uint16_t* src_ = xa + (kr_ + 16 * rep) * d;                                    \
+      uint16_t* row_ = dst_ + (2 * wave + 16 * rep) * HT;                                  \
+      const bool rin_ = k_begin + kr_ + 16 * rep + crow < k_end;                           \
+      if (full_ || (rin_ && a_col)) dma_row(row_, src_, voff);                              \
+      else *reinterpret_cast<uint4*>(row_ + 8 * lane) = make_uint4(0u, 0u, 0u, 0u);         \
+      if (!diag) {                                                                         \
+        if (full_ || (rin_ && b_col)) dma_row(row_ + PANEL, src_ + jdelta, voff);           \
+        else *reinterpret_cast<uint4*>(row_ + PANEL + 8 * lane) = make_uint4(0u, 0u, 0u, 0u); \
+      }                                                                                    \
+    }                                                                                      \
   } while (0)
 
-#define QZ_COMPUTE(CUR)                                                                    \
-  {                                                                                        \
-    const uint16_t* as = CUR;                                                              \
-    const uint16_t* bs = diag ? CUR : CUR + PANEL;                                         \
-    _Pragma("unroll") for (int ks = 0; ks < HBK; ks += 16) {                               \
-      bf16x8 a[2], b[4];                                                                   \
-      _Pragma("unroll") for (int mt = 0; mt < 2; ++mt)                                     \
-        a[mt] = operand_swz(as, wm * 64 + mt * 32, ks, lane);                              \
-      _Pragma("unroll") for (int nt = 0; nt < 4; ++nt)                                     \
-        b[nt] = operand_swz(bs, wn * 128 + nt * 32, ks, lane);                             \
-      _Pragma("unroll") for (int mt = 0; mt < 2; ++mt)                                     \
-        _Pragma("unroll") for (int nt = 0; nt < 4; ++nt)                                   \
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt], b[nt], acc[mt][nt],  \
-                                                                0, 0, 0);                  \
-    }                                                                                      \
-  }
+#define QZ_RD(off) __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4_ptr)(lbase + (off)))
+#define QZ_OP(off)                                                                         \
+  __builtin_bit_cast(bf16x8, __builtin_shufflevector(QZ_RD(off), QZ_RD((off) + 8 * HT),    \
+                                                     0, 1, 2, 3, 4, 5, 6, 7))
+#define QZ_LOAD(BUF, ks, RA, RB)                                                           \
+  do {                                                                                     \
+    constexpr uint32_t c_ = (BUF) * 4 * PANEL + 2 * (ks) * HT;                              \
+    _Pragma("unroll") for (int mt = 0; mt < 2; ++mt) RA[mt] = QZ_OP(aoff[mt] + c_);         \
+    _Pragma("unroll") for (int nt = 0; nt < 4; ++nt) RB[nt] = QZ_OP(boffs[nt] + c_);        \
+  } while (0)
 
-// vmcnt(0) (the pair's DMA landed) and lgkmcnt(0) (zero fills and this wave's LDS reads
-// done), then the workgroup barrier.  s_waitcnt 0x0070: vmcnt 0, expcnt 7, lgkmcnt 0.
-// The stage count is rounded up to even (a stage past the token range is zero-filled and
-// adds nothing), so both stages of a pair run without a branch between them and the
-// compiler can read the second stage's operands while the first stage's MFMAs run.
-#define QZ_PAIR(kk, C0, C1, N0, N1)                                                        \
-  if ((kk) < nke) {                                                                        \
+#define QZ_MFMA(RA, RB)                                                                    \
+  do {                                                                                     \
+    _Pragma("unroll") for (int mt = 0; mt < 2; ++mt)                                       \
+      _Pragma("unroll") for (int nt = 0; nt < 4; ++nt)                                     \
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(RA[mt], RB[nt], acc[mt][nt],  \
+                                                              0, 0, 0);                    \
+  } while (0)
+
+// The scheduling fences keep each step's reads ahead of the previous step's MFMAs (the
+// compiler would otherwise sink them and reuse one register set).  Before the barrier:
+// vmcnt(0) (the next pair's copies landed) and lgkmcnt(0) (zero fills and this wave's
+// LDS reads done); s_waitcnt 0x0070 = vmcnt 0, expcnt 7, lgkmcnt 0.
+#define QZ_FENCE __builtin_amdgcn_sched_barrier(0)
+#define QZ_PAIR(pp, C0, C1, N0)                                                            \
+  if ((pp) < np) {                                                                         \
+    QZ_LOAD(C0, 16, ra1, rb1);                                                             \
+    QZ_FENCE;                                                                              \
+    QZ_MFMA(ra0, rb0);                                                                     \
+    QZ_FENCE;                                                                              \
+    QZ_LOAD(C1, 0, ra0, rb0);                                                              \
+    QZ_FENCE;                                                                              \
+    QZ_MFMA(ra1, rb1);                                                                     \
+    QZ_FENCE;                                                                              \
+    QZ_LOAD(C1, 16, ra1, rb1);                                                             \
+    QZ_FENCE;                                                                              \
+    QZ_MFMA(ra0, rb0);                                                                     \
+    QZ_FENCE;                                                                              \
     __builtin_amdgcn_s_waitcnt(0x0070);                                                    \
     __builtin_amdgcn_s_barrier();                                                          \
-    if ((kk) + 2 < nke) {                                                                  \
-      QZ_ISSUE(N0, (kk) + 2);                                                              \
-      QZ_ISSUE(N1, (kk) + 3);                                                              \
+    if ((pp) + 1 < np) QZ_LOAD(N0, 0, ra0, rb0);                                           \
+    QZ_FENCE;                                                                              \
+    QZ_MFMA(ra1, rb1);                                                                     \
+    QZ_FENCE;                                                                              \
+    if ((pp) + 2 < np) {                                                                   \
+      QZ_ISSUE(C0, 2 * ((pp) + 2));                                                        \
+      QZ_ISSUE(C1, 2 * ((pp) + 2) + 1);                                                    \
     }                                                                                      \
-    QZ_COMPUTE(C0)                                                                         \
-    QZ_COMPUTE(C1)                                                                         \
   }
 
-  const int64_t nke = nk + (nk & 1);
-  if (0 < nke) {
-    QZ_ISSUE(L0, 0);
-    QZ_ISSUE(L1, 1);
+  if (np > 0) {
+    QZ_ISSUE(0, 0);
+    QZ_ISSUE(1, 1);
+    if (np > 1) {
+      QZ_ISSUE(2, 2);
+      QZ_ISSUE(3, 3);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070);
+    __builtin_amdgcn_s_barrier();
+    QZ_LOAD(0, 0, ra0, rb0);
   }
-  for (int64_t kt = 0; kt < nke; kt += NSTAGE) {
-    QZ_PAIR(kt + 0, L0, L1, L2, L3)
-    QZ_PAIR(kt + 2, L2, L3, L0, L1)
+  for (int64_t p = 0; p < np; p += 2) {
+    QZ_PAIR(p, 0, 1, 2)
+    QZ_PAIR(p + 1, 2, 3, 0)
   }
 #undef QZ_PAIR
-#undef QZ_COMPUTE
+#undef QZ_FENCE
+#undef QZ_MFMA
+#undef QZ_LOAD
+#undef QZ_OP
+#undef QZ_RD
 #undef QZ_ISSUE
 
   float* out = g.partial + (split * g.n_tiles + t) * (static_cast<int64_t>(HT) * HT);
@@ -490,7 +597,6 @@ __global__ __launch_bounds__(kSmall) void transpose_f32_kernel(const float* __re
   }
 }
 
-constexpr int64_t kSlots = 256;   // resident workgroups: one per CU
 
 // Token splits: the smallest S whose rounds of kSlots workgroups waste at most 2% more
 // than the best S <= 32 (each workgroup's work shrinks as 1/S).
