@@ -41,14 +41,14 @@ PEAK_FP64 = 78.6e12        # vector / matrix fp64, FLOP/s
 # SHA-256 of the kernel's source file at the time.  A kernel whose source has changed
 # since reports null.
 TRAFFIC = {
-    "gemm_admm_wupdate1": (5005.4e6, "k_gemm.hip",
+    "gemm_admm_wupdate1": (5017.3e6, "k_gemm.hip",
                           "4b3b79ff82303147030bf74c271647bb946e67de79935df19ec0b3d93bad1e6a"),
-    "gemm_admm_wupdate2": (6754.2e6, "k_gemm.hip",
+    "gemm_admm_wupdate2": (6745.2e6, "k_gemm.hip",
                           "4b3b79ff82303147030bf74c271647bb946e67de79935df19ec0b3d93bad1e6a"),
     "admm_project": (932.4e6, "k_admm.hip",
                     "e3f70300b61a47cdee85889e1ec3a8654dbc49310bc60d5cd8d2f4e4b4851f12"),
-    "hessian_gram_bf16": (16956.8e6, "k_hessian.hip",
-                         "723de72bd9990e911405d47a4ffaee907167f22ebeaa77f904a64d02ddb86363"),
+    "hessian_gram_bf16": (14376.3e6, "k_hessian.hip",
+                         "d766119e693b64cf85da12bd79f782a06930585ddb6025f63b8b90050119261c"),
 }
 TRAFFIC_WORKLOAD = "up_4096x12288_w3g128"
 
