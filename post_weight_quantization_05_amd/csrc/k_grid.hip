@@ -195,6 +195,37 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const uint8_t* __restric
   }
 }
 
+// Rows of a multiple of 32 codes, 16-byte aligned: 32 codes fill exactly BITS words of
+// the row's bit stream (32 BITS bits), so each thread reads one 32-code unit as two
+// 16-byte vectors and writes its BITS words; the shifts are compile-time constants.
+// Thread t handles unit t % units of row t / units (total < 2^31, 32-bit indices).
+template <int BITS>
+__global__ __launch_bounds__(kThreads) void pack32_kernel(const uint8_t* __restrict__ codes,
+                                                          uint32_t units, uint32_t total,
+                                                          uint32_t* __restrict__ out) {
+  constexpr uint32_t mask = (1u << BITS) - 1u;
+  for (uint32_t t = blockIdx.x * blockDim.x + threadIdx.x; t < total; t += gridDim.x * blockDim.x) {
+    const uint32_t r = t / units, u = t - r * units;
+    const uint8_t* src = codes + (static_cast<int64_t>(r) * units + u) * 32;
+    const uint4 a = *reinterpret_cast<const uint4*>(src);
+    const uint4 b = *reinterpret_cast<const uint4*>(src + 16);
+    const uint32_t in[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint32_t w[BITS];
+#pragma unroll
+    for (int k = 0; k < BITS; ++k) w[k] = 0u;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t c = (in[i >> 2] >> (8 * (i & 3))) & mask;
+      const int pos = i * BITS, wi = pos >> 5, sh = pos & 31;
+      w[wi] |= c << sh;
+      if (sh + BITS > 32) w[wi + 1] |= c >> (32 - sh);
+    }
+    uint32_t* dst = out + (static_cast<int64_t>(r) * units + u) * BITS;
+#pragma unroll
+    for (int k = 0; k < BITS; ++k) dst[k] = w[k];
+  }
+}
+
 // One thread per code.
 __global__ __launch_bounds__(kThreads) void unpack_kernel(const uint32_t* __restrict__ in,
                                                           int64_t rows, int64_t cols, int bits,
@@ -395,6 +426,22 @@ int launch_pack(const uint8_t* codes, int64_t rows, int64_t cols, int bits, uint
   const int64_t words = ceil_div(cols * bits, 32);
   const int64_t n = rows * words;
   if (n == 0) return QZ_OK;
+  const int64_t units = cols / 32;
+  if (cols % 32 == 0 && reinterpret_cast<uintptr_t>(codes) % 16 == 0 &&
+      rows * units < (int64_t{1} << 31) && bits >= 1 && bits <= 8) {
+    const uint32_t total = static_cast<uint32_t>(rows * units);
+    const unsigned grid = blocks_for(total, kThreads, 65536);
+    switch (bits) {
+#define QZ_PACK32(B)                                                                           \
+  case B:                                                                                      \
+    pack32_kernel<B><<<grid, kThreads, 0, s>>>(codes, static_cast<uint32_t>(units), total, out); \
+    break;
+      QZ_PACK32(1) QZ_PACK32(2) QZ_PACK32(3) QZ_PACK32(4)
+      QZ_PACK32(5) QZ_PACK32(6) QZ_PACK32(7) QZ_PACK32(8)
+#undef QZ_PACK32
+    }
+    return check_launch("pack32");
+  }
   pack_kernel<<<blocks_for(n, kThreads, 65536), kThreads, 0, s>>>(codes, rows, cols, bits, words, out);
   return check_launch("pack");
 }

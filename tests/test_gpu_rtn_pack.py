@@ -62,7 +62,7 @@ def test_rtn_rejects_nonfinite():
 
 
 @pytest.mark.parametrize("bits", list(range(1, 9)))
-@pytest.mark.parametrize("cols", [1, 11, 128, 131])
+@pytest.mark.parametrize("cols", [1, 11, 32, 128, 131, 4096])
 def test_pack_bit_exact(bits, cols):
     q = qz()
     codes = np.random.default_rng(bits * 100 + cols).integers(0, 1 << bits, (9, cols)).astype(np.uint8)
@@ -80,6 +80,22 @@ def test_pack_golden(case):
     words = q.qz_pack(to_dev(codes), case["bits"])
     np.testing.assert_array_equal(to_host(words).view(np.uint32),
                                   np.array(case["words"], np.uint64).astype(np.uint32))
+
+
+@pytest.mark.parametrize("offset", [1, 16])
+@pytest.mark.parametrize("bits", [3, 5, 8])
+def test_pack_code_alignment(offset, bits):
+    # rows of 64 codes starting 1 byte (the per-word kernel) or 16 bytes (the 32-code
+    # unit kernel) into an allocation: the same words either way
+    q = qz()
+    import torch
+    rows, cols = 7, 64
+    codes = np.random.default_rng(offset * 10 + bits).integers(0, 1 << bits, (rows, cols)).astype(np.uint8)
+    buf = torch.zeros(offset + rows * cols, dtype=torch.uint8, device="cuda")
+    view = buf[offset:].view(rows, cols)
+    view.copy_(torch.from_numpy(codes).cuda())
+    words = q.qz_pack(view, bits)
+    np.testing.assert_array_equal(to_host(words).view(np.uint32), pack.pack(codes, bits))
 
 
 def test_pack_full_size_roundtrip():
