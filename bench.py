@@ -48,7 +48,7 @@ TRAFFIC = {
     "admm_project": (932.4e6, "k_admm.hip",
                     "e3f70300b61a47cdee85889e1ec3a8654dbc49310bc60d5cd8d2f4e4b4851f12"),
     "hessian_gram_bf16": (14376.3e6, "k_hessian.hip",
-                         "d766119e693b64cf85da12bd79f782a06930585ddb6025f63b8b90050119261c"),
+                         "2a1ccf1ce62306db32ddea42ac13c0a6dcc82e25da215221220577df49397698"),
 }
 TRAFFIC_WORKLOAD = "up_4096x12288_w3g128"
 

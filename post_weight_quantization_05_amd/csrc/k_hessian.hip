@@ -198,59 +198,18 @@ __global__ __launch_bounds__(kThreads, 1) void gram_bf16_kernel(const HArgs g) {
 // cores work on the current 64.  LDS rows are one token of 256 channels (512 B, no padding);
 // the 32-byte chunk c of row r is stored at chunk c ^ (2 (r & 3)), which keeps both
 // the transpose reads (4 rows x 2 chunks per half wave) and the DMA writes free of
-// bank conflicts.
+// bank conflicts: element (token k, channel m) of a panel sits at
+// k HT + 16 ((m >> 4) ^ (2 (k & 3))) + (m & 15).
 constexpr int NSTAGE = 4;
 constexpr int PANEL = HBK * HT;   // bf16 elements per panel per stage
-
-__device__ __forceinline__ int swz(int k, int m) {   // element offset of (token k, channel m)
-  return k * HT + 16 * ((m >> 4) ^ (2 * (k & 3))) + (m & 15);
-}
-
-__device__ __forceinline__ bf16x8 operand_swz(const uint16_t* tile, int c0, int kb0, int lane) {
-  const int g = lane >> 4, s = lane & 15;
-  const int m = c0 + 16 * (g & 1) + 4 * (s & 3);
-  const int k = kb0 + 8 * (g >> 1) + (s >> 2);
-  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4_ptr)(tile + swz(k, m)));
-  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4_ptr)(tile + swz(k + 4, m)));
-  typedef short v8i16 __attribute__((ext_vector_type(8)));
-  const v8i16 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, both);
-}
-
-// One stage of one panel: 32 token rows = 16 row pairs; wavefront w copies pairs w, w+8.
-__device__ __forceinline__ void dma_panel(uint16_t* dst, const uint16_t* __restrict__ X,
-                                          int64_t k0, int64_t k_end, int64_t col0, int64_t d,
-                                          int wave, int lane) {
-#pragma unroll
-  for (int rep = 0; rep < 2; ++rep) {
-    const int r0 = 2 * (wave + 8 * rep);
-    const int r = r0 + (lane >> 5);
-    const int q = lane & 31;
-    const int c = (q >> 1) ^ (2 * (r & 3));
-    const int64_t grow = k0 + r;
-    const int64_t gcol = col0 + 16 * c + 8 * (q & 1);
-    uint16_t* base = dst + r0 * HT;
-    if (grow < k_end && gcol < d) {
-      // Issued as inline asm so that the compiler does not treat it as an LDS write it
-      // must wait for before every later LDS read: the stages are synchronised by the
-      // explicit vmcnt waits below.  The instruction has no register result.
-      const uint32_t lds_off = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
-          reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint16_t*)base)));
-      const uint16_t* src = X + grow * d + gcol;
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-                   :
-                   : "s"(lds_off), "v"(src)
-                   : "memory", "m0");
-    } else {
-      *reinterpret_cast<uint4*>(base + 8 * lane) = make_uint4(0u, 0u, 0u, 0u);
-    }
-  }
-}
 
 // Stage copy: lane l of wavefront w copies, for each of the two row halves (rep), token
 // row 2w + l/32 + 16 rep and the 16-byte piece that lands at byte 16 (l mod 32) of that
 // LDS row under the chunk swizzle.  The source is a wave-uniform base in scalar
-// registers plus one 32-bit lane offset that is the same for every stage and panel.  In
+// registers plus one 32-bit lane offset that is the same for every stage and panel.  It is
+// issued as inline asm so that the compiler does not treat it as an LDS write it must wait
+// for before every later LDS read (the stages are synchronised by the explicit vmcnt waits
+// before each barrier); the instruction has no register result.  In
 // a stage that lies wholly inside X every lane copies; otherwise lanes whose token row is
 // at or past k_end, or whose 8 channels are at or past d, write zeros instead (with
 // d % 8 == 0 a 16-byte piece is wholly inside or wholly outside).
