@@ -411,6 +411,13 @@ __global__ __launch_bounds__(kThreads) void chol_trailing(double* __restrict__ A
   tile_update<false>(A, lda, i0, j0, A, lda, i0, k0, A, lda, k0, j0);
 }
 
+// The same update for one block column c only: tiles (c + blockIdx.x, c).
+__global__ __launch_bounds__(kThreads) void chol_trailing_col(double* __restrict__ A, int64_t lda,
+                                                              int64_t k, int64_t c) {
+  const int64_t i0 = (c + static_cast<int64_t>(blockIdx.x)) * NB, j0 = c * NB, k0 = k * NB;
+  tile_update<false>(A, lda, i0, j0, A, lda, i0, k0, A, lda, k0, j0);
+}
+
 // Rows below block k:  A[i][k-block] <- A[i][k-block] * Dinv_k^T, in place.  16 rows per
 // workgroup, one 16 x 16 output block per wavefront (16 v_mfma_f64_16x16x4 along K), the
 // fragments read straight from global memory (A_op[m][q] from row r0 + m, B_op[q][n] =
@@ -614,11 +621,13 @@ namespace {
 // Look-ahead schedule.  The caller's stream runs the critical chain: per block column
 // k the panel below diagonal block k, then one launch (col_diag) that updates block
 // column k + 1 and factors diagonal block k + 1.  A second stream applies block column k
-// to the rest of the trailing matrix (columns >= k + 2) while the chain moves on; a third
+// to the rest of the trailing matrix (columns >= k + 2, column k + 2 first, the chain's next
+// step waiting only for that column) while the chain moves on; a third
 // runs inverse step k (X row block k and its update of the rows below) as soon as the
-// panel of k is done.  The update of column k + 1 waits for the previous step's rest
-// update, so every tile still receives its updates in order of k, and the results are
-// those of the one-stream order.
+// panel of k is done.  The update of column k + 1 waits for the previous step's update of
+// that column, which the rest-update stream runs after every earlier rest update, so every
+// tile still receives its updates in order of k, and the results are those of the
+// one-stream order.
 int factor_reversed(const float* H, int64_t d, const int32_t* perm, double* A, int64_t dp,
                     double* Dinv, double* diag0, double* X, uint32_t* flag, hipStream_t s) {
   const int64_t nblk = dp / NB;
@@ -665,17 +674,25 @@ int factor_reversed(const float* H, int64_t d, const int32_t* perm, double* A, i
     QZ_TRY(fork(s_trail, la ? la->ev_panel : nullptr));
     if (X) QZ_TRY(fork(s_inv, la ? la->ev_panel : nullptr));
     if (below > 0) {
-      if (k > 0) QZ_TRY(fork(s, la ? la->ev_trail : nullptr));   // rest update of k - 1 done
+      if (k > 0) QZ_TRY(fork(s, la ? la->ev_trail : nullptr));   // column k + 1 by panel k - 1
       col_diag<<<static_cast<unsigned>(below), kThreads, kStepPadBytes, s>>>(A, dp, k, diag0, Dinv,
                                                                            flag);
       QZ_TRY(check_launch("rfactor.coldiag"));
     }
+    // Rest update by panel k: block column k + 2 first (the next step's col_diag waits for
+    // it, and through the stream for the earlier rest updates), then the columns after it,
+    // which have two chain steps to finish before the step that needs them.
     if (below > 1) {
-      chol_trailing<<<static_cast<unsigned>((below - 1) * below / 2), kThreads, 0, s_trail>>>(
-          A, dp, k, k + 2);
-      QZ_TRY(check_launch("rfactor.trailing"));
+      chol_trailing_col<<<static_cast<unsigned>(below - 1), kThreads, 0, s_trail>>>(A, dp, k,
+                                                                                  k + 2);
+      QZ_TRY(check_launch("rfactor.trailing_col"));
     }
     QZ_TRY(mark(la ? la->ev_trail : nullptr, s_trail));
+    if (below > 2) {
+      chol_trailing<<<static_cast<unsigned>((below - 2) * (below - 1) / 2), kThreads, 0,
+                      s_trail>>>(A, dp, k, k + 3);
+      QZ_TRY(check_launch("rfactor.trailing"));
+    }
     if (X) {
       inv_rowscale<<<static_cast<unsigned>(k + 1), kThreads, 0, s_inv>>>(X, dp, k, Dinv);
       QZ_TRY(check_launch("rfactor.rowscale"));
