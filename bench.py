@@ -41,13 +41,13 @@ PEAK_FP64 = 78.6e12        # vector / matrix fp64, FLOP/s
 # SHA-256 of the kernel's source file at the time.  A kernel whose source has changed
 # since reports null.
 TRAFFIC = {
-    "gemm_admm_wupdate1": (5017.3e6, "k_gemm.hip",
+    "gemm_admm_wupdate1": (5004.4e6, "k_gemm.hip",
                           "4b3b79ff82303147030bf74c271647bb946e67de79935df19ec0b3d93bad1e6a"),
-    "gemm_admm_wupdate2": (6745.2e6, "k_gemm.hip",
+    "gemm_admm_wupdate2": (6754.9e6, "k_gemm.hip",
                           "4b3b79ff82303147030bf74c271647bb946e67de79935df19ec0b3d93bad1e6a"),
     "admm_project": (932.4e6, "k_admm.hip",
                     "e3f70300b61a47cdee85889e1ec3a8654dbc49310bc60d5cd8d2f4e4b4851f12"),
-    "hessian_gram_bf16": (14376.3e6, "k_hessian.hip",
+    "hessian_gram_bf16": (14558.0e6, "k_hessian.hip",
                          "2a1ccf1ce62306db32ddea42ac13c0a6dcc82e25da215221220577df49397698"),
 }
 TRAFFIC_WORKLOAD = "up_4096x12288_w3g128"
