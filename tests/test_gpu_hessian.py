@@ -14,7 +14,10 @@ from oracle import hessian
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("n,d", [(3000, 200), (512, 128), (4096, 77), (64, 8), (130, 300)])
+# (5003, 520) and (2077, 776): several 256-wide tiles on the direct-copy path with a ragged
+# last tile column (8 channels at d = 776) and a token count that ends inside a stage
+@pytest.mark.parametrize("n,d", [(3000, 200), (512, 128), (4096, 77), (64, 8), (130, 300),
+                                 (5003, 520), (2077, 776)])
 def test_hessian_bf16_small(n, d):
     q = qz()
     X = qz_synth.calib_bf16(5, n, d, p_out=0.02, f_out=30.0)
